@@ -1,0 +1,281 @@
+"""Benchmark of the W8A8 INT8 Linear hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload up_proj]
+
+One step = one pass of the whole per-call path over one batch of synthetic
+activations, with the weights quantised once beforehand (the init-time step,
+timed separately and reported, not part of a step):
+
+  up_proj   (default)  RMSNorm+per-token quant [28672 x 4096] ->
+                       INT8 GEMM + post-scale vs W [16384 x 4096] -> BF16
+  down_proj            per-token quant [32760 x 13824] -> GEMM vs W [5120 x 13824]
+  square               per-token quant [4096 x 4096] -> GEMM vs W [4096 x 4096]
+  blockwise_small/large  1x128 quant [1000|32760 x 5120] -> blockwise GEMM vs
+                       128x128-quantised W [5120 x 5120]
+
+Prints ONE JSON line: whole-step INT8 throughput (TOP/s, 2*M*N*K ops per
+step), the per-kernel roofline of the dominant kernel (the GEMM, against the
+5.0 POP/s dense INT8 MFMA peak), the quant kernel's HBM bandwidth, and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W8A8 GEMM INT8 TOPS + % INT8 MFMA peak at DiT FFN shapes; quant GB/s"
+INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, TOP/s
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+N_ROTATE = 3                   # activation buffers cycled so inputs come from HBM
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="up_proj")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-bf16", action="store_true", help="skip the torch BF16 Linear yardstick")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "w8a8_int8_quantized_token_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str, src_hash: str):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None
+    if there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the W8A8 Linear is "
+              "token-parallel and needs no collectives; see DESIGN.md for how it would shard.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import w8a8_int8_quantized_token_amd as w8
+
+    wl = W.WORKLOADS[args.workload]
+    M, N, K = wl.M, wl.N, wl.K
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t0 = time.perf_counter()
+    x_host = W.x_bits(wl)
+    w_host = W.w_bits(wl)
+    gamma = up(W.gamma_bits(wl)) if wl.norm else None
+    xs = [up(x_host)]
+    for _ in range(N_ROTATE - 1):
+        xs.append(xs[0].clone())
+    w_bf16 = up(w_host)
+    gen_s = time.perf_counter() - t0
+
+    # ---- init-time weight quantisation (not part of a step) -----------------
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    if wl.blockwise:
+        qw, sw = w8.w8a8_quant_rows(w_bf16, 128, 128)
+    else:
+        qw, sw = w8.w8a8_quant_rows(w_bf16)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    wquant_ms = ev[0].elapsed_time(ev[1])
+
+    qa = torch.empty((M, K), dtype=torch.int8, device=dev)
+    if wl.blockwise:
+        sa = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    else:
+        sa = torch.empty((M,), dtype=torch.float32, device=dev)
+    inv = torch.empty((M,), dtype=torch.float32, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    if wl.norm:
+        quant_name = "rmsnorm_quant"
+        def quant(x):
+            w8.w8a8_rmsnorm_quant(x, gamma, wl.eps, q=qa, scale=sa, inv_rms=inv)
+        quant_bytes = 3 * M * K + 4 * M + 2 * K + 4 * M     # read x, gamma; write q, scale, inv_rms
+    elif wl.blockwise:
+        quant_name = "quant_rows_1x128"
+        def quant(x):
+            w8.w8a8_quant_rows(x, 1, 128, q=qa, scale=sa)
+        quant_bytes = 3 * M * K + 4 * M * (K // 128)
+    else:
+        quant_name = "quant_rows"
+        def quant(x):
+            w8.w8a8_quant_rows(x, q=qa, scale=sa)
+        quant_bytes = 3 * M * K + 4 * M
+
+    if wl.blockwise:
+        gemm_name = "gemm_blockwise"
+        def gemm():
+            w8.w8a8_gemm_blockwise(qa, qw, sa, sw, out=out)
+    else:
+        gemm_name = "gemm_postscale"
+        def gemm():
+            w8.w8a8_gemm_postscale(qa, qw, sa, sw, out=out)
+
+    ops = 2 * M * N * K
+    for i in range(args.warmup):
+        quant(xs[i % N_ROTATE])
+        gemm()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        e = evs[i]
+        e[0].record(stream)
+        quant(xs[i % N_ROTATE])
+        e[1].record(stream)
+        gemm()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_start
+    quant_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    gemm_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
+    ms_per_step = wall_s * 1e3 / args.steps
+
+    gemm_avg = float(gemm_ms.mean())
+    gemm_tops = ops / (gemm_avg * 1e-3) / 1e12
+    quant_avg = float(quant_ms.mean())
+    quant_gbs = quant_bytes / (quant_avg * 1e-3) / 1e9
+    value = ops / (ms_per_step * 1e-3) / 1e12
+
+    gemm_hash = source_hash("gemm.hip", "device_common.hpp")
+    traffic = load_traffic(gemm_name, args.workload, gemm_hash)
+
+    extra = {
+        "gemm_ms_avg": round(gemm_avg, 4), "gemm_ms_min": round(float(gemm_ms.min()), 4),
+        "gemm_tops": round(gemm_tops, 1), "gemm_frac_int8_peak": round(gemm_tops / INT8_PEAK_TOPS, 4),
+        f"{quant_name}_ms_avg": round(quant_avg, 4), f"{quant_name}_gbs": round(quant_gbs, 1),
+        f"{quant_name}_frac_hbm_peak": round(quant_gbs / HBM_PEAK_GBS, 4),
+        "event_step_ms_avg": round(float(step_ms.mean()), 4),
+        "weight_quant_ms": round(wquant_ms, 4), "input_gen_s": round(gen_s, 1),
+    }
+
+    # ---- the pages' yardstick: torch's BF16 Linear on the same shape ---------
+    if not args.no_bf16:
+        wt = w_bf16
+        for i in range(3):
+            torch.nn.functional.linear(xs[i % N_ROTATE], wt)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record(stream)
+        for i in range(reps):
+            torch.nn.functional.linear(xs[i % N_ROTATE], wt)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bf16_ms = e0.elapsed_time(e1) / reps
+        extra["torch_bf16_linear_ms"] = round(bf16_ms, 4)
+        extra["speedup_vs_bf16_linear"] = round(bf16_ms / float(step_ms.mean()), 3)
+
+    # ---- CPU oracle on a bounded sample of the same workload -----------------
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl, x_host, w_host, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "N": N, "K": K,
+                   "step": f"{quant_name}+{gemm_name}", "weights": "int8, quantised at init"},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": INT8_PEAK_TOPS,
+                     "unit": "TOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
+                     "traffic": traffic, "kernel": gemm_name, "ops_per_launch": ops},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(wl, x_host, w_host, budget_s):
+    """The oracle, as it stands, on as many leading rows as fit the time budget."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    t0 = time.perf_counter()
+    if wl.blockwise:
+        qw, sw = O.quantize_groups(w_host, 128, 128)
+    else:
+        qw, sw = O.quantize_rows(w_host)
+    t_w = time.perf_counter() - t0
+    rows_done = 0
+    chunk = 256
+    t_path = 0.0
+    g = None
+    if wl.norm:
+        import workloads as W
+        g = W.gamma_bits(wl)
+    while rows_done < wl.M and t_path < budget_s:
+        r1 = min(rows_done + chunk, wl.M)
+        x = x_host[rows_done:r1]
+        t1 = time.perf_counter()
+        if wl.norm:
+            qa, sa, _ = O.rmsnorm_quant(x, g, wl.eps)
+            O.postscale_bf16(O.gemm_i32(qa, qw), sa, sw)
+        elif wl.blockwise:
+            qa, sa = O.quantize_groups(x, 1, 128)
+            O.gemm_blockwise_bf16(qa, sa, qw, sw)
+        else:
+            qa, sa = O.quantize_rows(x)
+            O.postscale_bf16(O.gemm_i32(qa, qw), sa, sw)
+        t_path += time.perf_counter() - t1
+        rows_done = r1
+        chunk = min(chunk * 2, 4096)
+    ops = 2 * rows_done * wl.N * wl.K
+    return {"value": round(ops / t_path / 1e12, 5), "unit": "TOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"first {rows_done} of {wl.M} token rows through the whole per-call path "
+                      f"({t_path:.1f} s); weight quant of all {wl.N} rows took {t_w:.1f} s, excluded"}
+
+
+if __name__ == "__main__":
+    main()

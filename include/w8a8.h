@@ -1,0 +1,176 @@
+/*
+ * w8a8.h -- C ABI of the MI355X (gfx950) W8A8 INT8 Linear library.
+ *
+ * The operation (from "TurboDiffusion Integration Notes", TurboT2AV
+ * docs/acceleration.md):
+ *   - section "Reused Components", W8A8 Linear bullet: weights are quantised
+ *     to INT8 once, when the model is initialised; activations are quantised
+ *     dynamically right before every transformer Linear; shapes the INT8 path
+ *     does not cover run on a retained BF16 weight with the native Linear;
+ *   - section "Reused Components", FastNorm bullet: RMSNorm is replaced by a
+ *     fused implementation (here: fused in front of the activation quant);
+ *   - section "Differences From TurboDiffusion", W8A8-kernel row and the
+ *     paragraph under the table: the post-scale kernel keeps one integer
+ *     accumulation running across all of K and applies the activation and
+ *     weight scales in the epilogue; the original kernel was blockwise-scaled.
+ *
+ * Conventions shared by every entry point:
+ *   - Every data pointer is a DEVICE pointer, owned by the caller. The library
+ *     allocates nothing, keeps no state between calls and never synchronises.
+ *   - Row-major layouts; leading dimensions (ld*) are in ELEMENTS.
+ *   - BF16 values travel as their 16-bit patterns (uint16_t).
+ *   - `stream` is a hipStream_t passed as an opaque pointer (NULL = the
+ *     legacy null stream). Work is enqueued on it; the call returns before it
+ *     runs.
+ *   - Arguments are validated on the host before anything is enqueued. On any
+ *     status other than W8A8_OK nothing was launched and no output was
+ *     written; w8a8_last_error() then describes the problem.
+ *   - Inputs are assumed finite (NaN/Inf give unspecified codes). Outputs
+ *     must not overlap inputs. Calls are thread-safe.
+ *   - A call with zero rows (rows == 0 or M == 0) is valid and does nothing;
+ *     its pointers may then be NULL (the other arguments are still checked).
+ *
+ * Quantisation readings (the pages leave the formula open):
+ *   scale = fl32(absmax / 127) over the group; code = round-half-even(
+ *   fl32(x / scale)) clamped to [-127, 127]; an all-zero group has scale 0
+ *   and codes 0. Scales are fp32.
+ */
+#ifndef W8A8_H
+#define W8A8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W8A8_OK = 0,
+  /* null pointer, negative size, ld smaller than the row, overlapping
+     output, non-finite or negative eps */
+  W8A8_ERR_INVALID_ARGUMENT = 1,
+  /* a shape or alignment the INT8 kernels do not cover: the caller should
+     fall back to its BF16 Linear ("Reused Components", W8A8 Linear bullet) */
+  W8A8_ERR_UNSUPPORTED_SHAPE = 2,
+  /* the HIP runtime reported an error while launching */
+  W8A8_ERR_HIP = 3
+} w8a8_status_t;
+
+/* Largest K for which 127*127*K fits an INT32 accumulator, rounded down to a
+   multiple of 128. */
+#define W8A8_MAX_K 133120
+
+/*
+ * w8a8_quant_rows -- symmetric absmax INT8 quantisation of a BF16 matrix.
+ *
+ * Passage: "Reused Components", W8A8 Linear bullet (activations quantised
+ * dynamically before each Linear; weights quantised once at initialisation);
+ * the (1,128) and (128,128) groups are the blockwise scheme of the original
+ * TurboDiffusion kernel ("Differences From TurboDiffusion", W8A8 kernel row).
+ *
+ *   x      [rows, cols] BF16, row stride ldx            (input)
+ *   q      [rows, cols] int8, row stride ldq            (output)
+ *   scale  fp32 [ceil(rows/group_rows), cols/group_cols], dense row-major
+ *                                                        (output)
+ * Supported groups:
+ *   (1, cols)   one scale per row: per-token activations, or per-output-
+ *               channel weights when x is the [N, K] weight;
+ *   (1, 128)    per token per 128-wide K block (blockwise activations);
+ *   (128, 128)  per 128x128 block (blockwise weights); the last row group
+ *               may be ragged.
+ * Requirements (else W8A8_ERR_UNSUPPORTED_SHAPE): cols % 8 == 0, and
+ * cols % 128 == 0 for the 128-wide groups; x and q 16-byte aligned; ldx % 8
+ * == 0 and ldq % 8 == 0; scale 4-byte aligned.
+ */
+w8a8_status_t w8a8_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                              int64_t group_rows, int64_t group_cols,
+                              int8_t* q, int64_t ldq, float* scale, void* stream);
+
+/*
+ * w8a8_rmsnorm_quant -- RMSNorm prologue fused with per-token quantisation.
+ *
+ * Passage: "Reused Components", FastNorm bullet (fused RMSNorm) composed with
+ * the W8A8 Linear bullet's dynamic activation quantisation.
+ *
+ *   r[m]  = fl32(1 / sqrt(mean_k x[m,k]^2 + eps))   (sum of squares in fp64)
+ *   y     = bf16(fl32(fl32(x * r) * gamma[k]))       (never leaves the chip)
+ *   q, scale = per-token quantisation of y, as w8a8_quant_rows (1, cols).
+ *
+ *   x       [rows, cols] BF16, stride ldx  (input)
+ *   gamma   [cols] BF16                    (input)
+ *   q       [rows, cols] int8, stride ldq  (output)
+ *   scale   [rows] fp32                    (output)
+ *   inv_rms [rows] fp32 r, or NULL         (optional output)
+ * Requirements as w8a8_quant_rows with group (1, cols); gamma 16-byte aligned;
+ * eps finite and >= 0 (else W8A8_ERR_INVALID_ARGUMENT).
+ */
+w8a8_status_t w8a8_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps,
+                                 int64_t rows, int64_t cols, int64_t ldx,
+                                 int8_t* q, int64_t ldq, float* scale, float* inv_rms,
+                                 void* stream);
+
+/*
+ * w8a8_gemm_postscale -- INT8 x INT8 GEMM, INT32 accumulation over all of K,
+ * fp32 post-scale epilogue, BF16 output.
+ *
+ * Passage: "Differences From TurboDiffusion", W8A8-kernel row and the
+ * paragraph under the table (continuous accumulation across K, activation and
+ * weight scales applied in the epilogue).
+ *
+ *   out[m,n] = bf16(fl32(fl32(fl32(acc[m,n]) * a_scale[m]) * w_scale[n])),
+ *   acc[m,n] = sum_k a[m,k] * w[n,k]   (exact INT32)
+ *
+ *   a       [M, K] int8, stride lda (activation codes)
+ *   w       [N, K] int8, stride ldw (weight codes, nn.Linear layout)
+ *   a_scale [M] fp32, w_scale [N] fp32
+ *   out     [M, N] BF16, stride ldo (output)
+ * Requirements (else W8A8_ERR_UNSUPPORTED_SHAPE): K % 128 == 0, 128 <= K <=
+ * W8A8_MAX_K, N % 128 == 0; a, w, out 16-byte aligned; lda % 16 == 0,
+ * ldw % 16 == 0, ldo % 8 == 0; scales 4-byte aligned. M >= 0 arbitrary.
+ */
+w8a8_status_t w8a8_gemm_postscale(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
+                                  const float* a_scale, const float* w_scale,
+                                  uint16_t* out, int64_t ldo,
+                                  int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * w8a8_gemm_blockwise -- blockwise-scaled W8A8 GEMM (the original
+ * TurboDiffusion scheme, "Differences From TurboDiffusion", W8A8 kernel row).
+ *
+ * For each 128-wide K block kb, in ascending order:
+ *   acc_kb = exact INT32 block sum; s = fl32(a_scale[m,kb] * w_scale[n/128,kb]);
+ *   c = fmaf(fl32(acc_kb), s, c)            (c starts at 0)
+ * out[m,n] = bf16(c).
+ *
+ *   a_scale [M, K/128] fp32 dense; w_scale [N/128, K/128] fp32 dense.
+ * Other arguments and requirements as w8a8_gemm_postscale.
+ */
+w8a8_status_t w8a8_gemm_blockwise(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
+                                  const float* a_scale, const float* w_scale,
+                                  uint16_t* out, int64_t ldo,
+                                  int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * w8a8_gemm_i32 -- the post-scale GEMM's main loop with the raw INT32
+ * accumulators as output (out[m,n] = sum_k a[m,k] * w[n,k]), so the integer
+ * part of the path can be checked bit for bit. Same passage and requirements
+ * as w8a8_gemm_postscale, with out int32 [M, N], ldo % 4 == 0.
+ */
+w8a8_status_t w8a8_gemm_i32(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
+                            int32_t* out, int64_t ldo,
+                            int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Static description of a status code. */
+const char* w8a8_status_string(w8a8_status_t s);
+
+/* Description of the last error on the calling thread ("" if none). */
+const char* w8a8_last_error(void);
+
+/* Library version string. */
+const char* w8a8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H */

@@ -1,0 +1,211 @@
+"""Python binding of the MI355X (gfx950) W8A8 INT8 Linear library.
+
+Thin ctypes marshalling over ``libw8a8.so`` (declared in include/w8a8.h):
+every function below has the name of the C entry point it calls, takes torch
+tensors that already live in device memory, passes their data pointers, sizes
+and strides plus torch's current HIP stream, and raises on a non-zero status.
+All arithmetic happens in the HIP kernels; torch only supplies device memory
+and the stream. If the library is missing, importing this package fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "W8A8Error", "W8A8Unsupported", "lib", "LIB_PATH", "EXPORTED_SYMBOLS",
+    "w8a8_quant_rows", "w8a8_rmsnorm_quant", "w8a8_gemm_postscale",
+    "w8a8_gemm_blockwise", "w8a8_gemm_i32", "w8a8_version",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw8a8.so")
+
+W8A8_OK = 0
+W8A8_ERR_INVALID_ARGUMENT = 1
+W8A8_ERR_UNSUPPORTED_SHAPE = 2
+W8A8_ERR_HIP = 3
+W8A8_MAX_K = 133120
+
+
+class W8A8Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class W8A8Unsupported(W8A8Error):
+    """The shape is outside what the INT8 kernels cover; use a BF16 Linear."""
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m w8a8_int8_quantized_token_amd.build` "
+        "(or __graft_entry__.build()). There is no fallback path.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+_st = ctypes.c_int
+
+_SIGS = {
+    "w8a8_quant_rows": [_p, _i64, _i64, _i64, _i64, _i64, _p, _i64, _p, _p],
+    "w8a8_rmsnorm_quant": [_p, _p, ctypes.c_float, _i64, _i64, _i64, _p, _i64, _p, _p, _p],
+    "w8a8_gemm_postscale": [_p, _i64, _p, _i64, _p, _p, _p, _i64, _i64, _i64, _i64, _p],
+    "w8a8_gemm_blockwise": [_p, _i64, _p, _i64, _p, _p, _p, _i64, _i64, _i64, _i64, _p],
+    "w8a8_gemm_i32": [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p],
+}
+for _name, _args in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _st
+_lib.w8a8_status_string.argtypes = [_st]
+_lib.w8a8_status_string.restype = ctypes.c_char_p
+_lib.w8a8_last_error.argtypes = []
+_lib.w8a8_last_error.restype = ctypes.c_char_p
+_lib.w8a8_version.argtypes = []
+_lib.w8a8_version.restype = ctypes.c_char_p
+
+EXPORTED_SYMBOLS = tuple(_SIGS) + ("w8a8_status_string", "w8a8_last_error", "w8a8_version")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raw ctypes handle, for tests of the ABI itself)."""
+    return _lib
+
+
+def w8a8_version() -> str:
+    return _lib.w8a8_version().decode()
+
+
+def _check(status: int, name: str) -> None:
+    if status == W8A8_OK:
+        return
+    msg = f"{name}: {_lib.w8a8_status_string(status).decode()}: {_lib.w8a8_last_error().decode()}"
+    if status == W8A8_ERR_UNSUPPORTED_SHAPE:
+        raise W8A8Unsupported(status, msg)
+    raise W8A8Error(status, msg)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _mat(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, f"{name} must be a row-major 2-D matrix")
+    return t
+
+
+def _vec(t: torch.Tensor, dtype: torch.dtype, n: int, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != dtype:
+        raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, f"{name} must be a {dtype} device tensor")
+    if t.numel() != n or not t.is_contiguous():
+        raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, f"{name} must be contiguous with {n} elements")
+    return t
+
+
+def _ld(t: torch.Tensor) -> int:
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], t.stride(0))
+
+
+def w8a8_quant_rows(x: torch.Tensor, group_rows: int = 1, group_cols: int | None = None,
+                    q: torch.Tensor | None = None, scale: torch.Tensor | None = None,
+                    stream=None):
+    """Symmetric absmax INT8 quantisation of a BF16 [rows, cols] matrix.
+
+    group (1, cols) (default): one scale per row; (1, 128): per 128-wide
+    block of each row; (128, 128): per 128x128 block. Returns (q, scale).
+    """
+    _mat(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    gc = cols if group_cols is None else group_cols
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    if scale is None:
+        n_gr = -(-rows // group_rows) if group_rows > 0 else 0
+        shape = (n_gr,) if (group_rows == 1 and gc == cols) else (n_gr, cols // gc if gc > 0 else 0)
+        scale = torch.empty(shape, dtype=torch.float32, device=x.device)
+    _mat(q, torch.int8, "q")
+    st = _lib.w8a8_quant_rows(_ptr(x), rows, cols, _ld(x), group_rows, gc, _ptr(q), _ld(q),
+                              _ptr(scale), _stream(stream))
+    _check(st, "w8a8_quant_rows")
+    return q, scale
+
+
+def w8a8_rmsnorm_quant(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
+                       q: torch.Tensor | None = None, scale: torch.Tensor | None = None,
+                       inv_rms: torch.Tensor | bool | None = True, stream=None):
+    """RMSNorm (gain gamma, no bias) fused with per-token INT8 quantisation.
+    Returns (q, scale, inv_rms) (inv_rms is None when not requested)."""
+    _mat(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    _vec(gamma, torch.bfloat16, cols, "gamma")
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    if scale is None:
+        scale = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    if inv_rms is True:
+        inv_rms = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    elif inv_rms is False:
+        inv_rms = None
+    _mat(q, torch.int8, "q")
+    st = _lib.w8a8_rmsnorm_quant(_ptr(x), _ptr(gamma), float(eps), rows, cols, _ld(x), _ptr(q),
+                                 _ld(q), _ptr(scale), _ptr(inv_rms), _stream(stream))
+    _check(st, "w8a8_rmsnorm_quant")
+    return q, scale, inv_rms
+
+
+def _gemm_args(a, w, out, out_dtype):
+    _mat(a, torch.int8, "a")
+    _mat(w, torch.int8, "w")
+    M, K = a.shape
+    N, K2 = w.shape
+    if K != K2:
+        raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, f"K mismatch: a has {K}, w has {K2}")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _mat(out, out_dtype, "out")
+    return M, N, K, out
+
+
+def w8a8_gemm_postscale(a: torch.Tensor, w: torch.Tensor, a_scale: torch.Tensor,
+                        w_scale: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    """out[M,N] (BF16) = bf16(acc * a_scale[m] * w_scale[n]), acc the exact
+    INT32 sum over K of a[m,k] * w[n,k]."""
+    M, N, K, out = _gemm_args(a, w, out, torch.bfloat16)
+    st = _lib.w8a8_gemm_postscale(_ptr(a), _ld(a), _ptr(w), _ld(w), _ptr(a_scale), _ptr(w_scale),
+                                  _ptr(out), _ld(out), M, N, K, _stream(stream))
+    _check(st, "w8a8_gemm_postscale")
+    return out
+
+
+def w8a8_gemm_blockwise(a: torch.Tensor, w: torch.Tensor, a_scale: torch.Tensor,
+                        w_scale: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    """Blockwise-scaled GEMM: a_scale [M, K/128], w_scale [N/128, K/128]."""
+    M, N, K, out = _gemm_args(a, w, out, torch.bfloat16)
+    st = _lib.w8a8_gemm_blockwise(_ptr(a), _ld(a), _ptr(w), _ld(w), _ptr(a_scale), _ptr(w_scale),
+                                  _ptr(out), _ld(out), M, N, K, _stream(stream))
+    _check(st, "w8a8_gemm_blockwise")
+    return out
+
+
+def w8a8_gemm_i32(a: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    """The post-scale GEMM's INT32 accumulators, out[m,n] = sum_k a[m,k] * w[n,k]."""
+    M, N, K, out = _gemm_args(a, w, out, torch.int32)
+    st = _lib.w8a8_gemm_i32(_ptr(a), _ld(a), _ptr(w), _ld(w), _ptr(out), _ld(out), M, N, K,
+                            _stream(stream))
+    _check(st, "w8a8_gemm_i32")
+    return out

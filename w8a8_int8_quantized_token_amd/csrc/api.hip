@@ -1,0 +1,210 @@
+// C ABI of the W8A8 library: host-side validation, then a launch on the
+// caller's stream. See include/w8a8.h for the contract of each entry point.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.hpp"
+#include "w8a8.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+w8a8_status_t fail(w8a8_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+w8a8_status_t ok() {
+  g_last_error.clear();
+  return W8A8_OK;
+}
+
+w8a8_status_t from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(W8A8_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Byte ranges [p, p + n) and [q, q + m) overlap?
+bool overlap(const void* p, size_t n, const void* q, size_t m) {
+  if (!p || !q || n == 0 || m == 0) return false;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + m && b < a + n;
+}
+
+// Bytes spanned by a row-major [rows, cols] matrix with row stride ld.
+size_t span_bytes(int64_t rows, int64_t cols, int64_t ld, size_t elem) {
+  if (rows <= 0 || cols <= 0) return 0;
+  return (size_t)((rows - 1) * ld + cols) * elem;
+}
+
+constexpr int64_t kMaxRows = 0x7FFFFFFF;
+
+w8a8_status_t check_quant_common(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                                 const void* q, int64_t ldq, const void* scale) {
+  if (rows < 0 || cols < 0) return fail(W8A8_ERR_INVALID_ARGUMENT, "negative size");
+  if (rows > kMaxRows) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "rows > 2^31-1");
+  if (cols == 0) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "cols must be positive");
+  if (ldx < cols || ldq < cols) return fail(W8A8_ERR_INVALID_ARGUMENT, "leading dimension < cols");
+  if (cols % 8) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "cols %% 8 != 0");
+  if (ldx % 8 || ldq % 8)
+    return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "ldx %% 8 and ldq %% 8 must be 0");
+  if (rows == 0) return W8A8_OK;          // nothing is read or written: pointers may be null
+  if (!x || !q || !scale) return fail(W8A8_ERR_INVALID_ARGUMENT, "null pointer");
+  if (!aligned(x, 16) || !aligned(q, 16))
+    return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "x and q must be 16-byte aligned");
+  if (!aligned(scale, 4)) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "scale must be 4-byte aligned");
+  return W8A8_OK;
+}
+
+w8a8_status_t check_gemm_common(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
+                                const void* out, int64_t ldo, size_t out_elem, int64_t M,
+                                int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return fail(W8A8_ERR_INVALID_ARGUMENT, "negative size");
+  if (lda < K || ldw < K || ldo < N)
+    return fail(W8A8_ERR_INVALID_ARGUMENT, "leading dimension smaller than the row");
+  if (K < 128 || K % 128) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "K must be a positive multiple of 128");
+  if (K > W8A8_MAX_K) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "K > %d overflows INT32", W8A8_MAX_K);
+  if (N < 128 || N % 128) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "N must be a positive multiple of 128");
+  if (M > kMaxRows || N > kMaxRows) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "M or N > 2^31-1");
+  if (lda % 16 || ldw % 16) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "lda and ldw must be multiples of 16");
+  if ((ldo * (int64_t)out_elem) % 16)
+    return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "output rows must start 16-byte aligned");
+  if (M == 0) return W8A8_OK;             // nothing is read or written: pointers may be null
+  if (!a || !w || !out) return fail(W8A8_ERR_INVALID_ARGUMENT, "null pointer");
+  if (!aligned(a, 16) || !aligned(w, 16) || !aligned(out, 16))
+    return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "a, w and out must be 16-byte aligned");
+  // Per-tile offsets are 32-bit: 256 rows of the larger operand stride.
+  if ((int64_t)256 * (lda > ldw ? lda : ldw) > 0x7FFFFFFF)
+    return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "leading dimension too large");
+  const size_t out_bytes = span_bytes(M, N, ldo, out_elem);
+  if (overlap(out, out_bytes, a, span_bytes(M, K, lda, 1)) ||
+      overlap(out, out_bytes, w, span_bytes(N, K, ldw, 1)))
+    return fail(W8A8_ERR_INVALID_ARGUMENT, "output overlaps an input");
+  return W8A8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w8a8_status_string(w8a8_status_t s) {
+  switch (s) {
+    case W8A8_OK: return "ok";
+    case W8A8_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case W8A8_ERR_UNSUPPORTED_SHAPE: return "unsupported shape (use the BF16 Linear)";
+    case W8A8_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* w8a8_last_error(void) { return g_last_error.c_str(); }
+
+const char* w8a8_version(void) { return "w8a8-gfx950 0.1"; }
+
+w8a8_status_t w8a8_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                              int64_t group_rows, int64_t group_cols, int8_t* q, int64_t ldq,
+                              float* scale, void* stream) {
+  w8a8_status_t st = check_quant_common(x, rows, cols, ldx, q, ldq, scale);
+  if (st != W8A8_OK) return st;
+  const bool per_row = group_rows == 1 && group_cols == cols;
+  const bool g1x128 = group_rows == 1 && group_cols == 128;
+  const bool g128x128 = group_rows == 128 && group_cols == 128;
+  if (!(per_row || g1x128 || g128x128))
+    return fail(W8A8_ERR_UNSUPPORTED_SHAPE,
+                "group (%lld, %lld) not supported: use (1, cols), (1, 128) or (128, 128)",
+                (long long)group_rows, (long long)group_cols);
+  if ((g1x128 || g128x128) && cols % 128)
+    return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "cols %% 128 != 0 for a 128-wide group");
+  const int64_t n_gr = (rows + group_rows - 1) / group_rows;
+  const size_t s_bytes = (size_t)(n_gr * (cols / group_cols)) * 4;
+  if (overlap(q, span_bytes(rows, cols, ldq, 1), x, span_bytes(rows, cols, ldx, 2)) ||
+      overlap(scale, s_bytes, x, span_bytes(rows, cols, ldx, 2)) ||
+      overlap(scale, s_bytes, q, span_bytes(rows, cols, ldq, 1)))
+    return fail(W8A8_ERR_INVALID_ARGUMENT, "outputs overlap each other or the input");
+  if (rows == 0) return ok();
+  return from_hip(w8a8::launch_quant_rows(x, rows, cols, ldx, group_rows, group_cols, q, ldq,
+                                          scale, (hipStream_t)stream),
+                  "w8a8_quant_rows launch");
+}
+
+w8a8_status_t w8a8_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps,
+                                 int64_t rows, int64_t cols, int64_t ldx, int8_t* q, int64_t ldq,
+                                 float* scale, float* inv_rms, void* stream) {
+  w8a8_status_t st = check_quant_common(x, rows, cols, ldx, q, ldq, scale);
+  if (st != W8A8_OK) return st;
+  if (!std::isfinite(eps) || eps < 0.0f) return fail(W8A8_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if (cols > w8a8::kRmsnormMaxCols)
+    return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "cols > %lld", (long long)w8a8::kRmsnormMaxCols);
+  if (rows == 0) return ok();
+  if (!gamma) return fail(W8A8_ERR_INVALID_ARGUMENT, "null gamma");
+  if (!aligned(gamma, 16)) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "gamma must be 16-byte aligned");
+  if (inv_rms && !aligned(inv_rms, 4)) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "inv_rms must be 4-byte aligned");
+  const size_t xb = span_bytes(rows, cols, ldx, 2), qb = span_bytes(rows, cols, ldq, 1);
+  if (overlap(q, qb, x, xb) || overlap(scale, (size_t)rows * 4, x, xb) ||
+      overlap(scale, (size_t)rows * 4, q, qb) || overlap(inv_rms, (size_t)rows * 4, x, xb) ||
+      overlap(inv_rms, (size_t)rows * 4, q, qb) || overlap(inv_rms, (size_t)rows * 4, scale, (size_t)rows * 4) ||
+      overlap(q, qb, gamma, (size_t)cols * 2))
+    return fail(W8A8_ERR_INVALID_ARGUMENT, "outputs overlap each other or an input");
+  if (rows == 0) return ok();
+  return from_hip(w8a8::launch_rmsnorm_quant(x, gamma, eps, rows, cols, ldx, q, ldq, scale, inv_rms,
+                                             (hipStream_t)stream),
+                  "w8a8_rmsnorm_quant launch");
+}
+
+w8a8_status_t w8a8_gemm_postscale(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
+                                  const float* a_scale, const float* w_scale, uint16_t* out,
+                                  int64_t ldo, int64_t M, int64_t N, int64_t K, void* stream) {
+  w8a8_status_t st = check_gemm_common(a, lda, w, ldw, out, ldo, 2, M, N, K);
+  if (st != W8A8_OK) return st;
+  if (M == 0) return ok();
+  if (!a_scale || !w_scale) return fail(W8A8_ERR_INVALID_ARGUMENT, "null scale pointer");
+  if (!aligned(a_scale, 4) || !aligned(w_scale, 4)) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "scales must be 4-byte aligned");
+  const size_t ob = span_bytes(M, N, ldo, 2);
+  if (overlap(out, ob, a_scale, (size_t)M * 4) || overlap(out, ob, w_scale, (size_t)N * 4))
+    return fail(W8A8_ERR_INVALID_ARGUMENT, "output overlaps a scale");
+  if (M == 0) return ok();
+  return from_hip(w8a8::launch_gemm(w8a8::Epilogue::kPostscaleBf16, a, lda, w, ldw, a_scale, w_scale,
+                                    out, ldo, M, N, K, (hipStream_t)stream),
+                  "w8a8_gemm_postscale launch");
+}
+
+w8a8_status_t w8a8_gemm_blockwise(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
+                                  const float* a_scale, const float* w_scale, uint16_t* out,
+                                  int64_t ldo, int64_t M, int64_t N, int64_t K, void* stream) {
+  w8a8_status_t st = check_gemm_common(a, lda, w, ldw, out, ldo, 2, M, N, K);
+  if (st != W8A8_OK) return st;
+  if (M == 0) return ok();
+  if (!a_scale || !w_scale) return fail(W8A8_ERR_INVALID_ARGUMENT, "null scale pointer");
+  if (!aligned(a_scale, 4) || !aligned(w_scale, 4)) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "scales must be 4-byte aligned");
+  const size_t ob = span_bytes(M, N, ldo, 2);
+  if (overlap(out, ob, a_scale, (size_t)M * (K / 128) * 4) ||
+      overlap(out, ob, w_scale, (size_t)(N / 128) * (K / 128) * 4))
+    return fail(W8A8_ERR_INVALID_ARGUMENT, "output overlaps a scale");
+  if (M == 0) return ok();
+  return from_hip(w8a8::launch_gemm(w8a8::Epilogue::kBlockwiseBf16, a, lda, w, ldw, a_scale, w_scale,
+                                    out, ldo, M, N, K, (hipStream_t)stream),
+                  "w8a8_gemm_blockwise launch");
+}
+
+w8a8_status_t w8a8_gemm_i32(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
+                            int32_t* out, int64_t ldo, int64_t M, int64_t N, int64_t K,
+                            void* stream) {
+  w8a8_status_t st = check_gemm_common(a, lda, w, ldw, out, ldo, 4, M, N, K);
+  if (st != W8A8_OK) return st;
+  if (M == 0) return ok();
+  return from_hip(w8a8::launch_gemm(w8a8::Epilogue::kInt32, a, lda, w, ldw, nullptr, nullptr, out,
+                                    ldo, M, N, K, (hipStream_t)stream),
+                  "w8a8_gemm_i32 launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,340 @@
+// Activation / weight quantisation kernels for gfx950.
+//
+// Per-token dynamic INT8 quantisation ("TurboDiffusion Integration Notes",
+// section "Reused Components", W8A8 Linear bullet) and its RMSNorm-fused form
+// (same section, FastNorm bullet). The path is HBM-bound: each row is read
+// once as BF16 and written once as INT8.
+//
+// Layout of the work: one 64-lane wave owns one row. Lane l holds 16-byte
+// vectors l, l+64, l+128, ... of the row (eight BF16 each), so every load
+// instruction of a wave reads 1 KiB of contiguous row data. The whole row
+// stays in registers between the absmax reduction and the quantisation, so
+// HBM sees it exactly once. Rows longer than the register budget fall back to
+// a two-pass loop that re-reads the row (from L2).
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace w8a8 {
+
+constexpr int kRowsPerBlock = 4;   // 4 waves of 64 lanes, one row each
+
+struct alignas(16) U4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ U4 load_nt(const U4* p) {
+  U4 v;
+  v.x = __builtin_nontemporal_load(&p->x);
+  v.y = __builtin_nontemporal_load(&p->y);
+  v.z = __builtin_nontemporal_load(&p->z);
+  v.w = __builtin_nontemporal_load(&p->w);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t absmax_u4(const U4& v, uint32_t m) {
+  m = absmax_bits_bf16x2(v.x, m);
+  m = absmax_bits_bf16x2(v.y, m);
+  m = absmax_bits_bf16x2(v.z, m);
+  return absmax_bits_bf16x2(v.w, m);
+}
+
+// Eight BF16 -> eight INT8 codes (two dwords).
+__device__ __forceinline__ uint2 quant_u4(const U4& v, const QuantParams& p) {
+  uint32_t c[8];
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[2 * i] = quant_code_bits(quant_quotient(bf16_lo(d[i]), p));
+    c[2 * i + 1] = quant_code_bits(quant_quotient(bf16_hi(d[i]), p));
+  }
+  return make_uint2(pack_codes(c[0], c[1], c[2], c[3]), pack_codes(c[4], c[5], c[6], c[7]));
+}
+
+// ---------------------------------------------------------------------------
+// Per-row (group (1, cols)) and per-128-block (group (1, 128)) quantisation,
+// row held in registers: kVpl 16-byte vectors per lane.
+// ---------------------------------------------------------------------------
+template <int kVpl, bool kGroup128>
+__global__ __launch_bounds__(kRowsPerBlock * kWave)
+void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+                       int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;                       // whole wave leaves together
+  const int nvec = (int)(cols >> 3);
+  const U4* xr = reinterpret_cast<const U4*>(x + row * ldx);
+  U4 v[kVpl];
+#pragma unroll
+  for (int j = 0; j < kVpl; ++j) {
+    const int idx = lane + j * kWave;
+    if (idx < nvec) v[j] = load_nt(xr + idx);
+    else v[j] = U4{0, 0, 0, 0};
+  }
+  uint2* qr = reinterpret_cast<uint2*>(q + row * ldq);
+  if constexpr (!kGroup128) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < kVpl; ++j) m = absmax_u4(v[j], m);
+    m = wave_max_u32(m);
+    const QuantParams p = quant_params(bf16_bits_to_float(m));
+#pragma unroll
+    for (int j = 0; j < kVpl; ++j) {
+      const int idx = lane + j * kWave;
+      if (idx < nvec) qr[idx] = quant_u4(v[j], p);
+    }
+    if (lane == 0) scale[row] = p.s;
+  } else {
+    // vector idx covers columns [8 idx, 8 idx + 8); 16 consecutive vectors
+    // (16 lanes) form one 128-wide group.
+    const int64_t ngroups = cols >> 7;
+#pragma unroll
+    for (int j = 0; j < kVpl; ++j) {
+      const int idx = lane + j * kWave;
+      uint32_t m = group_max_u32<16>(absmax_u4(v[j], 0u));
+      const QuantParams p = quant_params(bf16_bits_to_float(m));
+      if (idx < nvec) {
+        qr[idx] = quant_u4(v[j], p);
+        if ((lane & 15) == 0) scale[row * ngroups + (idx >> 4)] = p.s;
+      }
+    }
+  }
+}
+
+// Rows too long for the register-resident kernel: two passes over the row.
+template <bool kGroup128>
+__global__ __launch_bounds__(kRowsPerBlock * kWave)
+void quant_rows_long_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                            int64_t ldx, int8_t* __restrict__ q, int64_t ldq,
+                            float* __restrict__ scale) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int64_t nvec = cols >> 3;
+  const U4* xr = reinterpret_cast<const U4*>(x + row * ldx);
+  uint2* qr = reinterpret_cast<uint2*>(q + row * ldq);
+  if constexpr (!kGroup128) {
+    uint32_t m = 0;
+    for (int64_t idx = lane; idx < nvec; idx += kWave) m = absmax_u4(xr[idx], m);
+    m = wave_max_u32(m);
+    const QuantParams p = quant_params(bf16_bits_to_float(m));
+    for (int64_t idx = lane; idx < nvec; idx += kWave) qr[idx] = quant_u4(xr[idx], p);
+    if (lane == 0) scale[row] = p.s;
+  } else {
+    const int64_t ngroups = cols >> 7;
+    for (int64_t base = 0; base < nvec; base += kWave) {
+      const int64_t idx = base + lane;
+      const U4 v = idx < nvec ? xr[idx] : U4{0, 0, 0, 0};
+      uint32_t m = group_max_u32<16>(absmax_u4(v, 0u));
+      const QuantParams p = quant_params(bf16_bits_to_float(m));
+      if (idx < nvec) {
+        qr[idx] = quant_u4(v, p);
+        if ((lane & 15) == 0) scale[row * ngroups + (idx >> 4)] = p.s;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// (128, 128) groups: one workgroup of 256 threads per block of 128 rows x 128
+// columns (the last row group may be shorter). Used once per weight, when the
+// model is initialised.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256)
+void quant_block128_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                           int64_t ldx, int8_t* __restrict__ q, int64_t ldq,
+                           float* __restrict__ scale) {
+  __shared__ uint32_t red[4];
+  const int64_t gr = blockIdx.y, gc = blockIdx.x;
+  const int64_t r0 = gr * 128;
+  const int64_t nr = rows - r0 < 128 ? rows - r0 : 128;
+  // 128 rows x 16 vectors = 2048 vectors, 8 per thread
+  const int t = threadIdx.x;
+  U4 v[8];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = t + i * 256;
+    const int r = e >> 4, c = e & 15;
+    if (r < nr) {
+      v[i] = reinterpret_cast<const U4*>(x + (r0 + r) * ldx + gc * 128)[c];
+      m = absmax_u4(v[i], m);
+    } else {
+      v[i] = U4{0, 0, 0, 0};
+    }
+  }
+  m = wave_max_u32(m);
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  m = red[0];
+  for (int w = 1; w < 4; ++w) m = m > red[w] ? m : red[w];
+  const QuantParams p = quant_params(bf16_bits_to_float(m));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = t + i * 256;
+    const int r = e >> 4, c = e & 15;
+    if (r < nr) reinterpret_cast<uint2*>(q + (r0 + r) * ldq + gc * 128)[c] = quant_u4(v[i], p);
+  }
+  if (t == 0) scale[gr * (cols >> 7) + gc] = p.s;
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm + per-token quantisation, row in registers.
+//   r = fl32(1 / sqrt(sum(x^2) / K + eps)), the sum of exact squares in fp64;
+//   y = bf16(fl32(fl32(x * r) * gamma)); codes and scale from y.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double sumsq_u4(const U4& v, double acc) {
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const double a = (double)bf16_lo(d[i]);
+    const double b = (double)bf16_hi(d[i]);
+    acc = __builtin_fma(a, a, acc);
+    acc = __builtin_fma(b, b, acc);
+  }
+  return acc;
+}
+
+// y = bf16(fl32(fl32(x * r) * g)) for eight elements, repacked as BF16 pairs.
+__device__ __forceinline__ U4 rmsnorm_u4(const U4& v, const U4& g, float r) {
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  const uint32_t e[4] = {g.x, g.y, g.z, g.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = (bf16_lo(d[i]) * r) * bf16_lo(e[i]);
+    const float hi = (bf16_hi(d[i]) * r) * bf16_hi(e[i]);
+    o[i] = pack_bf16x2(lo, hi);
+  }
+  return U4{o[0], o[1], o[2], o[3]};
+}
+
+template <int kVpl>
+__global__ __launch_bounds__(kRowsPerBlock * kWave)
+void rmsnorm_quant_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
+                          float eps, int64_t rows, int64_t cols, int64_t ldx,
+                          int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale,
+                          float* __restrict__ inv_rms) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int nvec = (int)(cols >> 3);
+  const U4* xr = reinterpret_cast<const U4*>(x + row * ldx);
+  const U4* gr = reinterpret_cast<const U4*>(gamma);
+  U4 v[kVpl];
+  double ss = 0.0;
+#pragma unroll
+  for (int j = 0; j < kVpl; ++j) {
+    const int idx = lane + j * kWave;
+    if (idx < nvec) v[j] = load_nt(xr + idx);
+    else v[j] = U4{0, 0, 0, 0};
+    ss = sumsq_u4(v[j], ss);
+  }
+  ss = wave_sum_f64(ss);
+  const double r64 = 1.0 / __builtin_sqrt(ss / (double)cols + (double)eps);
+  const float r = (float)r64;
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < kVpl; ++j) {
+    const int idx = lane + j * kWave;
+    if (idx < nvec) {
+      v[j] = rmsnorm_u4(v[j], gr[idx], r);
+      m = absmax_u4(v[j], m);
+    }
+  }
+  m = wave_max_u32(m);
+  const QuantParams p = quant_params(bf16_bits_to_float(m));
+  uint2* qr = reinterpret_cast<uint2*>(q + row * ldq);
+#pragma unroll
+  for (int j = 0; j < kVpl; ++j) {
+    const int idx = lane + j * kWave;
+    if (idx < nvec) qr[idx] = quant_u4(v[j], p);
+  }
+  if (lane == 0) {
+    scale[row] = p.s;
+    if (inv_rms) inv_rms[row] = r;
+  }
+}
+
+template <int kVpl>
+static hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int64_t rows,
+                                 int64_t cols, int64_t ldx, int8_t* q, int64_t ldq, float* scale,
+                                 float* inv_rms, hipStream_t st) {
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  hipLaunchKernelGGL((rmsnorm_quant_kernel<kVpl>), grid, dim3(kRowsPerBlock * kWave), 0, st,
+                     x, gamma, eps, rows, cols, ldx, q, ldq, scale, inv_rms);
+  return hipGetLastError();
+}
+
+template <int kVpl, bool kG128>
+static hipError_t launch_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int8_t* q,
+                              int64_t ldq, float* scale, hipStream_t st) {
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  hipLaunchKernelGGL((quant_rows_kernel<kVpl, kG128>), grid, dim3(kRowsPerBlock * kWave), 0, st,
+                     x, rows, cols, ldx, q, ldq, scale);
+  return hipGetLastError();
+}
+
+// Smallest register-resident variant that holds `nvec` vectors per row, or 0.
+static int pick_vpl(int64_t nvec) {
+  static const int kChoices[] = {1, 2, 4, 8, 12, 16, 20, 24, 28, 32};
+  for (int c : kChoices)
+    if (nvec <= (int64_t)c * kWave) return c;
+  return 0;
+}
+
+#define W8A8_VPL_SWITCH(VPL, CALL) \
+  switch (VPL) {                    \
+    case 1: return CALL(1);         \
+    case 2: return CALL(2);         \
+    case 4: return CALL(4);         \
+    case 8: return CALL(8);         \
+    case 12: return CALL(12);       \
+    case 16: return CALL(16);       \
+    case 20: return CALL(20);       \
+    case 24: return CALL(24);       \
+    case 28: return CALL(28);       \
+    case 32: return CALL(32);       \
+    default: break;                 \
+  }
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                             int64_t group_rows, int64_t group_cols, int8_t* q, int64_t ldq,
+                             float* scale, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  if (group_rows == 128) {
+    const dim3 grid((unsigned)(cols >> 7), (unsigned)((rows + 127) / 128));
+    hipLaunchKernelGGL(quant_block128_kernel, grid, dim3(256), 0, st, x, rows, cols, ldx, q, ldq,
+                       scale);
+    return hipGetLastError();
+  }
+  // (1, 128) on a 128-wide matrix is the same as one group per row
+  const bool g128 = group_cols == 128 && cols != 128;
+  const int vpl = pick_vpl(cols >> 3);
+  if (!g128) {
+#define W8A8_CALL_ROW(V) launch_rows<V, false>(x, rows, cols, ldx, q, ldq, scale, st)
+    W8A8_VPL_SWITCH(vpl, W8A8_CALL_ROW)
+#undef W8A8_CALL_ROW
+    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+    hipLaunchKernelGGL((quant_rows_long_kernel<false>), grid, dim3(kRowsPerBlock * kWave), 0, st,
+                       x, rows, cols, ldx, q, ldq, scale);
+    return hipGetLastError();
+  }
+#define W8A8_CALL_G128(V) launch_rows<V, true>(x, rows, cols, ldx, q, ldq, scale, st)
+  W8A8_VPL_SWITCH(vpl, W8A8_CALL_G128)
+#undef W8A8_CALL_G128
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  hipLaunchKernelGGL((quant_rows_long_kernel<true>), grid, dim3(kRowsPerBlock * kWave), 0, st, x,
+                     rows, cols, ldx, q, ldq, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps, int64_t rows,
+                                int64_t cols, int64_t ldx, int8_t* q, int64_t ldq, float* scale,
+                                float* inv_rms, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const int vpl = pick_vpl(cols >> 3);
+#define W8A8_CALL_RMS(V) launch_rmsnorm<V>(x, gamma, eps, rows, cols, ldx, q, ldq, scale, inv_rms, st)
+  W8A8_VPL_SWITCH(vpl, W8A8_CALL_RMS)
+#undef W8A8_CALL_RMS
+  return hipErrorInvalidValue;   // host validation rejects longer rows first
+}
+
+}  // namespace w8a8
