@@ -47,7 +47,33 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-bf16", action="store_true", help="skip the torch BF16 Linear yardstick")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--copy-calib", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
+    p.add_argument("--summarize", metavar="PROF_DIR",
+                   help="summarise rocprofv3 results under PROF_DIR into profiles/ (no GPU)")
     return p.parse_args()
+
+
+def copy_calibration(steps: int) -> None:
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings scale
+    the counters of the W8A8 kernels, and its time is the achievable HBM rate."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dsts = [torch.empty_like(src) for _ in range(2)]
+    for d in dsts:
+        d.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        dsts[i % 2].copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copy_ms": round(ms, 4),
+                      "copy_gbs": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def source_hash(*names) -> str:
@@ -73,6 +99,15 @@ def load_traffic(kernel: str, workload: str, src_hash: str):
 
 def main():
     args = parse()
+    if args.summarize:
+        import profile_summary
+        profile_summary.main(args.summarize, os.path.join(ROOT, "profiles"),
+                             source_hash("gemm.hip", "device_common.hpp"),
+                             source_hash("quant.hip", "device_common.hpp"))
+        return
+    if args.copy_calib:
+        copy_calibration(args.steps)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the W8A8 Linear is "
               "token-parallel and needs no collectives; see DESIGN.md for how it would shard.",
