@@ -191,7 +191,9 @@ def test_rmsnorm_quant_no_inv_rms_and_stride():
 
 GEMM_SHAPES = [((64, 128, 256), 51), ((1, 128, 128), 52), ((1000, 384, 512), 53),
                ((257, 640, 1024), 54), ((4096, 4096, 4096), 55), ((129, 5120, 13824), 56),
-               ((300, 256, 128), 57), ((513, 1152, 640), 58)]
+               ((300, 256, 128), 57), ((513, 1152, 640), 58),
+               # more tiles than CUs: several tiles per persistent workgroup
+               ((4096, 16384, 256), 59), ((8292, 4096, 128), 60), ((2000, 3200, 384), 66)]
 
 
 @pytest.mark.parametrize("shape,seed", GEMM_SHAPES)

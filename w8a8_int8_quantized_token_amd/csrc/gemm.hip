@@ -276,11 +276,8 @@ hipError_t launch_gemm(Epilogue epi, const int8_t* a, int64_t lda, const int8_t*
   if (M == 0) return hipSuccess;
   switch (epi) {
     case Epilogue::kPostscaleBf16:
-      return launch_cfg<256, 256, 128, 64, 8, Epilogue::kPostscaleBf16>(
-          a, lda, w, ldw, a_scale, w_scale, out, ldo, M, N, K, st);
     case Epilogue::kInt32:
-      return launch_cfg<256, 256, 128, 64, 8, Epilogue::kInt32>(a, lda, w, ldw, a_scale, w_scale,
-                                                                out, ldo, M, N, K, st);
+      return launch_gemm_pipelined(epi, a, lda, w, ldw, a_scale, w_scale, out, ldo, M, N, K, st);
     case Epilogue::kBlockwiseBf16:
       return launch_cfg<256, 128, 128, 64, 8, Epilogue::kBlockwiseBf16>(
           a, lda, w, ldw, a_scale, w_scale, out, ldo, M, N, K, st);

@@ -1,0 +1,329 @@
+// Persistent, software-pipelined INT8 GEMM for gfx950 (post-scale and INT32
+// epilogues).
+//
+// "TurboDiffusion Integration Notes", section "Differences From
+// TurboDiffusion", paragraph under the table: one INT32 accumulation runs over
+// all of K; the activation and weight scales are applied in the epilogue.
+//
+// out[m, n] = epilogue( sum_k a[m, k] * w[n, k] ), a [M, K] and w [N, K] INT8,
+// both K-contiguous.
+//
+// Structure (one workgroup of 8 waves per CU, two waves per SIMD):
+//  * Block tile 256 (n) x 256 (m); each wave owns 128 x 64, held as 8 x 4
+//    v_mfma_i32_16x16x64_i8 accumulators (128 registers).
+//  * K is streamed in 128-byte stages through a 2-slot LDS ring (64 KiB per
+//    slot) filled by global_load_lds_dwordx4 (no register staging).
+//  * Fragments are read one 64-byte K step ahead into a second register set,
+//    so every MFMA finds its operands ready. The single stage barrier sits
+//    between the two K steps of a stage: after it, the next stage's first
+//    fragments are read and the slot just drained is refilled, both hidden
+//    behind the second K step's MFMAs.
+//  * The grid is persistent (one workgroup per CU) and walks its tiles back
+//    to back: the next tile's first stages are in flight during an epilogue.
+//    Workgroup b sits on XCD b % 8; each XCD owns a contiguous, M-grouped
+//    range of tiles so shared rows stay in that XCD's L2.
+//  * Weight rows are the MFMA "A" operand with permuted row slots so each
+//    lane ends up with 32 consecutive output channels of one token: the
+//    epilogue writes 64 contiguous bytes per token per lane.
+//  * LDS rows are XOR-swizzled in 16-byte chunks so each 8-lane phase of a
+//    ds_read_b128 touches 8 distinct 16-byte bank groups.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace w8a8 {
+namespace pipe {
+
+constexpr int kBN = 256, kBM = 256;   // block tile: output channels x tokens
+constexpr int kBK = 128;              // K bytes per stage (two 64-byte MFMA K steps)
+constexpr int kSlots = 2;             // LDS ring of stages
+constexpr int kSlotBytes = (kBN + kBM) * kBK;   // 64 KiB
+constexpr int kWaves = 8, kThreads = kWaves * kWave;
+constexpr int kTN = 8, kTM = 4;       // 16x16 MFMA tiles per wave: 128 channels x 64 tokens
+constexpr int kLoads = (kBN + kBM) * kBK / 1024 / kWaves;   // 1 KiB wave-loads per stage: 8
+constexpr int kStoresPerTile = kTM * 4;                       // 16-byte stores per wave per tile
+constexpr int kGroupM = 8;
+constexpr int kXcds = 8;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 128-byte LDS rows hold 8 chunks of 16 bytes; logical chunk c of row r sits
+// at c ^ key(r). Weight rows are read in the permuted slot order (rows r..r+3
+// and r+32..r+35 in one 8-lane phase), activation rows in order.
+__device__ __forceinline__ int key_w(int r) { return (r & 3) | (((r >> 5) & 1) << 2); }
+__device__ __forceinline__ int key_a(int r) { return r & 7; }
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// s_waitcnt vmcnt(n) for a run-time n, rounded down (waiting longer is safe).
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (n >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// This workgroup's tiles: logical ids start + k * stride, k < count.
+struct Sched {
+  int start, stride, count, tiles_m, tiles_n;
+};
+
+__device__ __forceinline__ Sched make_sched(int b, int grid, int tiles_m, int tiles_n) {
+  Sched s;
+  s.tiles_m = tiles_m;
+  s.tiles_n = tiles_n;
+  const int T = tiles_m * tiles_n;
+  const int x = b % kXcds, j = b / kXcds;
+  const int nwg = grid / kXcds + (x < grid % kXcds ? 1 : 0);     // workgroups on XCD x
+  const int tx = T / kXcds + (x < T % kXcds ? 1 : 0);            // tiles of XCD x
+  const int sx = x * (T / kXcds) + (x < T % kXcds ? x : T % kXcds);
+  s.start = sx + j;
+  s.stride = nwg;
+  s.count = j < tx ? (tx - j + nwg - 1) / nwg : 0;
+  return s;
+}
+
+// M-grouped order: groups of kGroupM tile rows, n fastest within a group.
+__device__ __forceinline__ void tile_mn(const Sched& s, int k, int& m0, int& n0) {
+  const int t = s.start + k * s.stride;
+  const int span = kGroupM * s.tiles_n;
+  const int g = t / span;
+  const int first = g * kGroupM;
+  const int gs = (s.tiles_m - first) < kGroupM ? (s.tiles_m - first) : kGroupM;
+  const int in = t - g * span;
+  m0 = (first + in % gs) * kBM;
+  n0 = (in / gs) * kBN;
+}
+
+__device__ __forceinline__ void mfma_all(v4i (&acc)[kTN][kTM], const v4i (&f)[kTN + kTM]) {
+#pragma unroll
+  for (int i = 0; i < kTN; ++i)
+#pragma unroll
+    for (int j = 0; j < kTM; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f[i], f[kTN + j], acc[i][j], 0, 0, 0);
+}
+
+template <Epilogue kEpi>
+__global__ __launch_bounds__(kThreads, 1)
+void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* __restrict__ w,
+                       int64_t ldw, const float* __restrict__ a_scale,
+                       const float* __restrict__ w_scale, void* __restrict__ out, int64_t ldo,
+                       int M, int N, int K, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) int8_t lds[kSlots * kSlotBytes];
+
+  const Sched sc = make_sched(blockIdx.x, gridDim.x, tiles_m, tiles_n);
+  const int nk = K / kBK;                       // stages per tile
+  const int total = sc.count * nk;              // stages of this workgroup
+  if (total == 0) return;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave & 1, wm = wave >> 1;
+
+  // ---- loader: wave-load g fills stage rows 8 (wave + 8 g) + [0, 8) (g < 4:
+  // weight rows, g >= 4: activation rows); lane -> row r_l + 64 g', physical
+  // chunk lane % 8, logical chunk fixed per lane (keys ignore bits >= 6).
+  const int r_l = 8 * wave + (lane >> 3);
+  const int p = lane & 7;
+  const int cw = (p ^ key_w(r_l)) << 4, ca = (p ^ key_a(r_l)) << 4;
+  int ld_k = 0, ld_kt = 0, ld_rvn = 0, ld_rvm = 0;
+  const int8_t* ld_wb = nullptr;
+  const int8_t* ld_ab = nullptr;
+  auto load_tile = [&](int k) {
+    int m0, n0;
+    tile_mn(sc, k, m0, n0);
+    ld_rvn = ((N - n0) < kBN ? (N - n0) : kBN) - 1;
+    ld_rvm = ((M - m0) < kBM ? (M - m0) : kBM) - 1;
+    ld_wb = w + (int64_t)n0 * ldw;
+    ld_ab = a + (int64_t)m0 * lda;
+  };
+  load_tile(0);
+  auto issue_next = [&](int slot) {
+    const int8_t* wb = ld_wb + ld_kt * kBK;
+    const int8_t* ab = ld_ab + ld_kt * kBK;
+    int8_t* dst = lds + slot * kSlotBytes + wave * 1024;
+#pragma unroll
+    for (int g = 0; g < kLoads / 2; ++g) {
+      int r = r_l + 64 * g;
+      r = r < ld_rvn ? r : ld_rvn;
+      __builtin_amdgcn_global_load_lds((const void*)(wb + (uint32_t)(r * (int)ldw + cw)),
+                                       (lds_void*)(dst + g * kWaves * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int g = 0; g < kLoads / 2; ++g) {
+      int r = r_l + 64 * g;
+      r = r < ld_rvm ? r : ld_rvm;
+      __builtin_amdgcn_global_load_lds((const void*)(ab + (uint32_t)(r * (int)lda + ca)),
+                                       (lds_void*)(dst + kBN * kBK + g * kWaves * 1024), 16, 0,
+                                       0);
+    }
+    if (++ld_kt == nk) {
+      ld_kt = 0;
+      if (++ld_k < sc.count) load_tile(ld_k);
+    }
+  };
+
+  // ---- fragments: MFMA row slot ir = lane % 16 of W tile i maps to wave-local
+  // channel 32 (ir / 4) + 4 i + ir % 4, so lane (ir, kq) ends up holding the 32
+  // consecutive channels 32 kq .. 32 kq + 31 of token ir + 16 j.
+  const int ir = lane & 15, kq = lane >> 4;
+  const int w_row0 = wn * 128 + 32 * (ir >> 2) + (ir & 3);
+  const int a_row0 = kBN + wm * (16 * kTM) + ir;
+  const int w_base = w_row0 * kBK, w_key = key_w(w_row0);
+  const int a_base = a_row0 * kBK, a_key = key_a(a_row0 - kBN);
+  auto read_frags = [&](v4i (&f)[kTN + kTM], int slot, int ks) {
+    const int8_t* sb = lds + slot * kSlotBytes;
+    const int cl = ks * 4 + kq;
+    const int wo = w_base + ((cl ^ w_key) << 4), ao = a_base + ((cl ^ a_key) << 4);
+#pragma unroll
+    for (int i = 0; i < kTN; ++i) f[i] = *reinterpret_cast<const v4i*>(sb + wo + i * 4 * kBK);
+#pragma unroll
+    for (int j = 0; j < kTM; ++j)
+      f[kTN + j] = *reinterpret_cast<const v4i*>(sb + ao + j * 16 * kBK);
+  };
+
+  v4i acc[kTN][kTM];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < kTN; ++i)
+#pragma unroll
+      for (int j = 0; j < kTM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+  };
+  zero_acc();
+  v4i f0[kTN + kTM], f1[kTN + kTM];
+
+  // ---- epilogue of tile k -----------------------------------------------------
+  auto epilogue = [&](int k) {
+    int m0, n0;
+    tile_mn(sc, k, m0, n0);
+    const int n_wave = n0 + wn * 128;
+    if (n_wave >= N) return;
+    const int n_lane = n_wave + 32 * kq;
+    const int m_lane = m0 + wm * (16 * kTM) + ir;
+    if constexpr (kEpi == Epilogue::kInt32) {
+      int32_t* o = reinterpret_cast<int32_t*>(out);
+#pragma unroll
+      for (int j = 0; j < kTM; ++j) {
+        const int m = m_lane + 16 * j;
+        if (m < M) {
+          int32_t* dst = o + (int64_t)m * ldo + n_lane;
+#pragma unroll
+          for (int i = 0; i < kTN; ++i) *reinterpret_cast<v4i*>(dst + 4 * i) = acc[i][j];
+        }
+      }
+    } else {
+      uint16_t* o = reinterpret_cast<uint16_t*>(out);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {          // two halves of 16 channels
+        float sw[2 * kTN];
+#pragma unroll
+        for (int e = 0; e < 2 * kTN; ++e) sw[e] = w_scale[n_lane + 16 * hf + e];
+#pragma unroll
+        for (int j = 0; j < kTM; ++j) {
+          // Rows past M hold exactly row M-1's sums (their loads were clamped
+          // to it), so they store row M-1's values to row M-1: every lane
+          // issues its stores and the per-tile store count stays fixed.
+          int m = m_lane + 16 * j;
+          m = m < M ? m : M - 1;
+          const float sa = a_scale[m];
+          uint32_t pk[kTN];
+#pragma unroll
+          for (int ii = 0; ii < kTN / 2; ++ii) {
+            const int i = (kTN / 2) * hf + ii;
+            const float v0 = ((float)acc[i][j][0] * sa) * sw[4 * ii + 0];
+            const float v1 = ((float)acc[i][j][1] * sa) * sw[4 * ii + 1];
+            const float v2 = ((float)acc[i][j][2] * sa) * sw[4 * ii + 2];
+            const float v3 = ((float)acc[i][j][3] * sa) * sw[4 * ii + 3];
+            pk[2 * ii] = pack_bf16x2(v0, v1);
+            pk[2 * ii + 1] = pack_bf16x2(v2, v3);
+          }
+          uint16_t* dst = o + (int64_t)m * ldo + n_lane + 16 * hf;
+          *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+          *reinterpret_cast<uint4*>(dst + 8) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+        }
+      }
+    }
+  };
+
+  // Stores of the previous tile's epilogue were issued after the next stage's
+  // loads; the barrier's vmcnt leaves them outstanding. They are counted only
+  // when every wave stores a full tile (N a multiple of 256); otherwise the
+  // wait covers them too, which is merely slower.
+  const int stores_per_tile = (kEpi != Epilogue::kInt32 && N % kBN == 0) ? kStoresPerTile : 0;
+  int pending_stores = 0;
+
+  // ---- prologue: stages 0 and 1 in flight; fragments of stage 0, K step 0 ----
+  int issued = 0;
+  for (; issued < kSlots && issued < total; ++issued) issue_next(issued);
+  wait_vmcnt_le(kLoads * (issued - 1));
+  lds_barrier();
+  read_frags(f0, 0, 0);
+
+  // ---- main loop: per stage, K step 0 from f0 (read one step ahead) and K
+  // step 1 from f1; the stage barrier sits between them. --------------------
+  int s = 0;
+  for (int k = 0; k < sc.count; ++k) {
+    for (int kt = 0; kt < nk; ++kt, ++s) {
+      const int slot = s & 1;
+      read_frags(f1, slot, 1);
+      mfma_all(acc, f0);
+      if (s + 1 < total) {
+        wait_lgkmcnt0();                   // this wave is done reading slot `slot`
+        wait_vmcnt_le(pending_stores);     // stage s+1 has landed
+        lds_barrier();                     // ... for every wave; slot `slot` is free
+        pending_stores = 0;
+        if (issued < total) {
+          issue_next(slot);                // stage s+2 reuses this slot
+          ++issued;
+        }
+        read_frags(f0, slot ^ 1, 0);
+      }
+      mfma_all(acc, f1);
+    }
+    epilogue(k);
+    if constexpr (kEpi == Epilogue::kInt32) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    pending_stores = stores_per_tile;
+    zero_acc();
+  }
+}
+
+}  // namespace pipe
+
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+hipError_t launch_gemm_pipelined(Epilogue epi, const int8_t* a, int64_t lda, const int8_t* w,
+                                 int64_t ldw, const float* a_scale, const float* w_scale,
+                                 void* out, int64_t ldo, int64_t M, int64_t N, int64_t K,
+                                 hipStream_t st) {
+  const int tiles_m = (int)((M + pipe::kBM - 1) / pipe::kBM);
+  const int tiles_n = (int)((N + pipe::kBN - 1) / pipe::kBN);
+  const int64_t tiles = (int64_t)tiles_m * tiles_n;
+  const int grid = (int)(tiles < cu_count() ? tiles : cu_count());
+  const dim3 block(pipe::kThreads);
+  if (epi == Epilogue::kInt32)
+    hipLaunchKernelGGL((pipe::gemm_i8_pipelined<Epilogue::kInt32>), dim3(grid), block, 0, st, a,
+                       lda, w, ldw, a_scale, w_scale, out, ldo, (int)M, (int)N, (int)K, tiles_m,
+                       tiles_n);
+  else
+    hipLaunchKernelGGL((pipe::gemm_i8_pipelined<Epilogue::kPostscaleBf16>), dim3(grid), block, 0,
+                       st, a, lda, w, ldw, a_scale, w_scale, out, ldo, (int)M, (int)N, (int)K,
+                       tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace w8a8
