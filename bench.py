@@ -36,6 +36,7 @@ METRIC = "W8A8 GEMM INT8 TOPS + % INT8 MFMA peak at DiT FFN shapes; quant GB/s"
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, TOP/s
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 N_ROTATE = 3                   # activation buffers cycled so inputs come from HBM
+GEMM_SOURCES = ("gemm.hip", "gemm_pipelined.hip", "device_common.hpp")
 
 
 def parse():
@@ -102,7 +103,7 @@ def main():
     if args.summarize:
         import profile_summary
         profile_summary.main(args.summarize, os.path.join(ROOT, "profiles"),
-                             source_hash("gemm.hip", "device_common.hpp"),
+                             source_hash(*GEMM_SOURCES),
                              source_hash("quant.hip", "device_common.hpp"))
         return
     if args.copy_calib:
@@ -210,7 +211,7 @@ def main():
     quant_gbs = quant_bytes / (quant_avg * 1e-3) / 1e9
     value = ops / (ms_per_step * 1e-3) / 1e12
 
-    gemm_hash = source_hash("gemm.hip", "device_common.hpp")
+    gemm_hash = source_hash(*GEMM_SOURCES)
     traffic = load_traffic(gemm_name, args.workload, gemm_hash)
 
     extra = {

@@ -42,7 +42,7 @@ WORKLOAD_SHAPES = {
 
 
 def short_name(kernel: str) -> str:
-    if "gemm_i8_kernel" in kernel:
+    if "gemm_i8_" in kernel:
         m = re.search(r"Epilogue\)(\d)|EpilogueE(\d)", kernel)
         e = (m.group(1) or m.group(2)) if m else "?"
         return {"0": "gemm_postscale", "1": "gemm_i32", "2": "gemm_blockwise"}.get(e, "gemm")
