@@ -95,13 +95,17 @@ __device__ __forceinline__ QuantParams quant_params(float amax) {
   return p;
 }
 
+// fl32(x / s): the reciprocal route (kFast, scale with a normal reciprocal)
+// or the IEEE division (tiny or zero scales).
+template <bool kFast>
 __device__ __forceinline__ float quant_quotient(float x, const QuantParams& p) {
-  if (p.fast) {
+  if constexpr (kFast) {
     float t = x * p.r;
     float e = __builtin_fmaf(-t, p.s, x);
     return __builtin_fmaf(e, p.r, t);
+  } else {
+    return p.s == 0.0f ? 0.0f : x / p.s;
   }
-  return p.s == 0.0f ? 0.0f : x / p.s;
 }
 
 // Low byte of the result is the INT8 code.

@@ -37,22 +37,64 @@ __device__ __forceinline__ uint32_t absmax_u4(const U4& v, uint32_t m) {
 }
 
 // Eight BF16 -> eight INT8 codes (two dwords).
+template <bool kFast>
 __device__ __forceinline__ uint2 quant_u4(const U4& v, const QuantParams& p) {
   uint32_t c[8];
   const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    c[2 * i] = quant_code_bits(quant_quotient(bf16_lo(d[i]), p));
-    c[2 * i + 1] = quant_code_bits(quant_quotient(bf16_hi(d[i]), p));
+    c[2 * i] = quant_code_bits(quant_quotient<kFast>(bf16_lo(d[i]), p));
+    c[2 * i + 1] = quant_code_bits(quant_quotient<kFast>(bf16_hi(d[i]), p));
   }
   return make_uint2(pack_codes(c[0], c[1], c[2], c[3]), pack_codes(c[4], c[5], c[6], c[7]));
 }
 
+__device__ __forceinline__ uint2 quant_u4(const U4& v, const QuantParams& p) {
+  return p.fast ? quant_u4<true>(v, p) : quant_u4<false>(v, p);
+}
+
+// Lane `lane` holds vectors lane + 64 j of the row (kFull: all of them exist).
+template <int kVpl, bool kFull>
+__device__ __forceinline__ bool has_vec(int lane, int j, int nvec) {
+  return kFull || lane + j * kWave < nvec;
+}
+
+// Quantise a register-resident row with one scale; the fast/slow choice is
+// uniform over the row, so it is taken once.
+template <int kVpl, bool kFull, bool kFast>
+__device__ __forceinline__ void store_row_codes(const U4 (&v)[kVpl], uint2* qr, int lane, int nvec,
+                                                const QuantParams& p) {
+#pragma unroll
+  for (int j = 0; j < kVpl; ++j)
+    if (has_vec<kVpl, kFull>(lane, j, nvec)) qr[lane + j * kWave] = quant_u4<kFast>(v[j], p);
+}
+
+// Unpredicated loads: a lane past the end of a short row re-reads the row's
+// last vector (always in bounds, nvec >= 1) and then zeroes it, so the loads
+// issue back to back with no branches around them.
+// kStream: data read once (non-temporal hint); otherwise a cached load.
+template <int kVpl, bool kFull, bool kStream = true>
+__device__ __forceinline__ void load_row(U4 (&v)[kVpl], const U4* xr, int lane, int nvec) {
+#pragma unroll
+  for (int j = 0; j < kVpl; ++j) {
+    const int idx = lane + j * kWave;
+    const U4* src = xr + (kFull || idx < nvec ? idx : nvec - 1);
+    if constexpr (kFull) {
+      v[j] = kStream ? load_nt(src) : *src;
+    } else {
+      const U4 t = kStream ? load_nt(src) : *src;
+      const bool in = idx < nvec;
+      v[j] = U4{in ? t.x : 0u, in ? t.y : 0u, in ? t.z : 0u, in ? t.w : 0u};
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Per-row (group (1, cols)) and per-128-block (group (1, 128)) quantisation,
-// row held in registers: kVpl 16-byte vectors per lane.
+// row held in registers: kVpl 16-byte vectors per lane. kFull: the row is
+// exactly kVpl * 64 vectors long, so no lane needs a bounds check.
 // ---------------------------------------------------------------------------
-template <int kVpl, bool kGroup128>
+template <int kVpl, bool kGroup128, bool kFull>
 __global__ __launch_bounds__(kRowsPerBlock * kWave)
 void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
                        int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale) {
@@ -62,12 +104,7 @@ void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t col
   const int nvec = (int)(cols >> 3);
   const U4* xr = reinterpret_cast<const U4*>(x + row * ldx);
   U4 v[kVpl];
-#pragma unroll
-  for (int j = 0; j < kVpl; ++j) {
-    const int idx = lane + j * kWave;
-    if (idx < nvec) v[j] = load_nt(xr + idx);
-    else v[j] = U4{0, 0, 0, 0};
-  }
+  load_row<kVpl, kFull>(v, xr, lane, nvec);
   uint2* qr = reinterpret_cast<uint2*>(q + row * ldq);
   if constexpr (!kGroup128) {
     uint32_t m = 0;
@@ -75,11 +112,8 @@ void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t col
     for (int j = 0; j < kVpl; ++j) m = absmax_u4(v[j], m);
     m = wave_max_u32(m);
     const QuantParams p = quant_params(bf16_bits_to_float(m));
-#pragma unroll
-    for (int j = 0; j < kVpl; ++j) {
-      const int idx = lane + j * kWave;
-      if (idx < nvec) qr[idx] = quant_u4(v[j], p);
-    }
+    if (p.fast) store_row_codes<kVpl, kFull, true>(v, qr, lane, nvec, p);
+    else store_row_codes<kVpl, kFull, false>(v, qr, lane, nvec, p);
     if (lane == 0) scale[row] = p.s;
   } else {
     // vector idx covers columns [8 idx, 8 idx + 8); 16 consecutive vectors
@@ -90,7 +124,7 @@ void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t col
       const int idx = lane + j * kWave;
       uint32_t m = group_max_u32<16>(absmax_u4(v[j], 0u));
       const QuantParams p = quant_params(bf16_bits_to_float(m));
-      if (idx < nvec) {
+      if (has_vec<kVpl, kFull>(lane, j, nvec)) {
         qr[idx] = quant_u4(v[j], p);
         if ((lane & 15) == 0) scale[row * ngroups + (idx >> 4)] = p.s;
       }
@@ -206,7 +240,7 @@ __device__ __forceinline__ U4 rmsnorm_u4(const U4& v, const U4& g, float r) {
   return U4{o[0], o[1], o[2], o[3]};
 }
 
-template <int kVpl>
+template <int kVpl, bool kFull>
 __global__ __launch_bounds__(kRowsPerBlock * kWave)
 void rmsnorm_quant_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
                           float eps, int64_t rows, int64_t cols, int64_t ldx,
@@ -218,81 +252,90 @@ void rmsnorm_quant_kernel(const uint16_t* __restrict__ x, const uint16_t* __rest
   const int nvec = (int)(cols >> 3);
   const U4* xr = reinterpret_cast<const U4*>(x + row * ldx);
   const U4* gr = reinterpret_cast<const U4*>(gamma);
+  // The row is streamed from HBM; the gains are L2-resident. Short rows load
+  // both up front; long rows (over 16 vectors per lane) fetch the gains in
+  // chunks after the reduction to stay within the register budget.
+  constexpr bool kGainsEarly = kVpl <= 16;
+  constexpr int kChunk = kGainsEarly ? kVpl : 8;
   U4 v[kVpl];
+  U4 g[kGainsEarly ? kVpl : kChunk];
+  load_row<kVpl, kFull>(v, xr, lane, nvec);
+  if constexpr (kGainsEarly) load_row<kVpl, kFull, false>(g, gr, lane, nvec);
   double ss = 0.0;
 #pragma unroll
-  for (int j = 0; j < kVpl; ++j) {
-    const int idx = lane + j * kWave;
-    if (idx < nvec) v[j] = load_nt(xr + idx);
-    else v[j] = U4{0, 0, 0, 0};
-    ss = sumsq_u4(v[j], ss);
-  }
+  for (int j = 0; j < kVpl; ++j) ss = sumsq_u4(v[j], ss);
   ss = wave_sum_f64(ss);
   const double r64 = 1.0 / __builtin_sqrt(ss / (double)cols + (double)eps);
   const float r = (float)r64;
   uint32_t m = 0;
 #pragma unroll
-  for (int j = 0; j < kVpl; ++j) {
-    const int idx = lane + j * kWave;
-    if (idx < nvec) {
-      v[j] = rmsnorm_u4(v[j], gr[idx], r);
+  for (int j0 = 0; j0 < kVpl; j0 += kChunk) {
+    if constexpr (!kGainsEarly) {
+#pragma unroll
+      for (int jj = 0; jj < kChunk; ++jj) {
+        const int idx = lane + (j0 + jj) * kWave;
+        if (j0 + jj < kVpl) g[jj] = gr[kFull || idx < nvec ? idx : nvec - 1];
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < kChunk && j0 + jj < kVpl; ++jj) {
+      const int j = j0 + jj;
+      v[j] = rmsnorm_u4(v[j], g[kGainsEarly ? j : jj], r);   // padding: x = 0 gives y = 0
       m = absmax_u4(v[j], m);
     }
   }
   m = wave_max_u32(m);
   const QuantParams p = quant_params(bf16_bits_to_float(m));
   uint2* qr = reinterpret_cast<uint2*>(q + row * ldq);
-#pragma unroll
-  for (int j = 0; j < kVpl; ++j) {
-    const int idx = lane + j * kWave;
-    if (idx < nvec) qr[idx] = quant_u4(v[j], p);
-  }
+  if (p.fast) store_row_codes<kVpl, kFull, true>(v, qr, lane, nvec, p);
+  else store_row_codes<kVpl, kFull, false>(v, qr, lane, nvec, p);
   if (lane == 0) {
     scale[row] = p.s;
     if (inv_rms) inv_rms[row] = r;
   }
 }
 
-template <int kVpl>
+template <int kVpl, bool kFull>
 static hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int64_t rows,
                                  int64_t cols, int64_t ldx, int8_t* q, int64_t ldq, float* scale,
                                  float* inv_rms, hipStream_t st) {
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-  hipLaunchKernelGGL((rmsnorm_quant_kernel<kVpl>), grid, dim3(kRowsPerBlock * kWave), 0, st,
+  hipLaunchKernelGGL((rmsnorm_quant_kernel<kVpl, kFull>), grid, dim3(kRowsPerBlock * kWave), 0, st,
                      x, gamma, eps, rows, cols, ldx, q, ldq, scale, inv_rms);
   return hipGetLastError();
 }
 
-template <int kVpl, bool kG128>
+template <int kVpl, bool kG128, bool kFull>
 static hipError_t launch_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, int8_t* q,
                               int64_t ldq, float* scale, hipStream_t st) {
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-  hipLaunchKernelGGL((quant_rows_kernel<kVpl, kG128>), grid, dim3(kRowsPerBlock * kWave), 0, st,
-                     x, rows, cols, ldx, q, ldq, scale);
+  hipLaunchKernelGGL((quant_rows_kernel<kVpl, kG128, kFull>), grid, dim3(kRowsPerBlock * kWave), 0,
+                     st, x, rows, cols, ldx, q, ldq, scale);
   return hipGetLastError();
 }
 
-// Smallest register-resident variant that holds `nvec` vectors per row, or 0.
+// Register-resident variants: vectors per lane. A row of nvec vectors takes
+// the smallest variant that holds it, the exact ("full", unpredicated) one
+// when nvec is a multiple of 64 in this list: K = 4096, 5120, 6144, 8192,
+// 13824 and 16384 all are.
 static int pick_vpl(int64_t nvec) {
-  static const int kChoices[] = {1, 2, 4, 8, 12, 16, 20, 24, 28, 32};
+  static const int kChoices[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 14, 16, 20, 24, 27, 28, 32};
   for (int c : kChoices)
     if (nvec <= (int64_t)c * kWave) return c;
   return 0;
 }
 
-#define W8A8_VPL_SWITCH(VPL, CALL) \
-  switch (VPL) {                    \
-    case 1: return CALL(1);         \
-    case 2: return CALL(2);         \
-    case 4: return CALL(4);         \
-    case 8: return CALL(8);         \
-    case 12: return CALL(12);       \
-    case 16: return CALL(16);       \
-    case 20: return CALL(20);       \
-    case 24: return CALL(24);       \
-    case 28: return CALL(28);       \
-    case 32: return CALL(32);       \
-    default: break;                 \
+#define W8A8_VPL_CASE(V, CALL) \
+  case V: return full ? CALL(V, true) : CALL(V, false);
+#define W8A8_VPL_SWITCH(VPL, CALL)                                                   \
+  switch (VPL) {                                                                     \
+    W8A8_VPL_CASE(1, CALL) W8A8_VPL_CASE(2, CALL) W8A8_VPL_CASE(3, CALL)             \
+    W8A8_VPL_CASE(4, CALL) W8A8_VPL_CASE(5, CALL) W8A8_VPL_CASE(6, CALL)             \
+    W8A8_VPL_CASE(8, CALL) W8A8_VPL_CASE(10, CALL) W8A8_VPL_CASE(12, CALL)           \
+    W8A8_VPL_CASE(14, CALL) W8A8_VPL_CASE(16, CALL) W8A8_VPL_CASE(20, CALL)          \
+    W8A8_VPL_CASE(24, CALL) W8A8_VPL_CASE(27, CALL) W8A8_VPL_CASE(28, CALL)          \
+    W8A8_VPL_CASE(32, CALL)                                                          \
+    default: break;                                                                  \
   }
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
@@ -308,8 +351,9 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int6
   // (1, 128) on a 128-wide matrix is the same as one group per row
   const bool g128 = group_cols == 128 && cols != 128;
   const int vpl = pick_vpl(cols >> 3);
+  const bool full = vpl > 0 && (cols >> 3) == (int64_t)vpl * kWave;
   if (!g128) {
-#define W8A8_CALL_ROW(V) launch_rows<V, false>(x, rows, cols, ldx, q, ldq, scale, st)
+#define W8A8_CALL_ROW(V, F) launch_rows<V, false, F>(x, rows, cols, ldx, q, ldq, scale, st)
     W8A8_VPL_SWITCH(vpl, W8A8_CALL_ROW)
 #undef W8A8_CALL_ROW
     const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
@@ -317,7 +361,7 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int6
                        x, rows, cols, ldx, q, ldq, scale);
     return hipGetLastError();
   }
-#define W8A8_CALL_G128(V) launch_rows<V, true>(x, rows, cols, ldx, q, ldq, scale, st)
+#define W8A8_CALL_G128(V, F) launch_rows<V, true, F>(x, rows, cols, ldx, q, ldq, scale, st)
   W8A8_VPL_SWITCH(vpl, W8A8_CALL_G128)
 #undef W8A8_CALL_G128
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
@@ -331,7 +375,9 @@ hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float 
                                 float* inv_rms, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   const int vpl = pick_vpl(cols >> 3);
-#define W8A8_CALL_RMS(V) launch_rmsnorm<V>(x, gamma, eps, rows, cols, ldx, q, ldq, scale, inv_rms, st)
+  const bool full = vpl > 0 && (cols >> 3) == (int64_t)vpl * kWave;
+#define W8A8_CALL_RMS(V, F) \
+  launch_rmsnorm<V, F>(x, gamma, eps, rows, cols, ldx, q, ldq, scale, inv_rms, st)
   W8A8_VPL_SWITCH(vpl, W8A8_CALL_RMS)
 #undef W8A8_CALL_RMS
   return hipErrorInvalidValue;   // host validation rejects longer rows first
