@@ -41,7 +41,12 @@ constexpr int kWaves = 8, kThreads = kWaves * kWave;
 constexpr int kTN = 8, kTM = 4;       // 16x16 MFMA tiles per wave: 128 channels x 64 tokens
 constexpr int kLoads = (kBN + kBM) * kBK / 1024 / kWaves;   // 1 KiB wave-loads per stage: 8
 constexpr int kStoresPerTile = kTM * 4;                       // 16-byte stores per wave per tile
+constexpr int kScaleBytes = (kBN + kBM) * 4;   // one tile's scales
+constexpr int kScaleBufs = 3;                  // tile k's scales sit in buffer k % 3
+constexpr int kScaleLoads = 1;                 // scale wave-loads per wave per tile
 constexpr int kGroupM = 8;
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
 constexpr int kXcds = 8;
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -62,8 +67,10 @@ __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcn
 
 // s_waitcnt vmcnt(n) for a run-time n, rounded down (waiting longer is safe).
 __device__ __forceinline__ void wait_vmcnt_le(int n) {
-  if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  if (n >= 17) asm volatile("s_waitcnt vmcnt(17)" ::: "memory");
+  else if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
   else if (n >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if (n >= 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
@@ -99,6 +106,26 @@ __device__ __forceinline__ void tile_mn(const Sched& s, int k, int& m0, int& n0)
   n0 = (in / gs) * kBN;
 }
 
+// LDS reads of the epilogue's scales. Written as instructions the compiler
+// does not analyse: otherwise it cannot tell them apart from the LDS targets
+// of the loads still in flight (global_load_lds) and waits for all of those
+// first, draining the pipeline at every tile. The data they read is
+// published by the stage barriers, and the caller waits for the reads.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+typedef float v4f __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4f lds_read_f4(uint32_t addr) {
+  v4f v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+__device__ __forceinline__ float lds_read_f1(uint32_t addr) {
+  float v;
+  asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+
 __device__ __forceinline__ void mfma_all(v4i (&acc)[kTN][kTM], const v4i (&f)[kTN + kTM]) {
 #pragma unroll
   for (int i = 0; i < kTN; ++i)
@@ -113,7 +140,9 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
                        int64_t ldw, const float* __restrict__ a_scale,
                        const float* __restrict__ w_scale, void* __restrict__ out, int64_t ldo,
                        int M, int N, int K, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) int8_t lds[kSlots * kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) int8_t lds[kSlots * kSlotBytes + kScaleBufs * kScaleBytes];
+  int8_t* const scale_bufs = lds + kSlots * kSlotBytes;
+  constexpr bool kScales = kEpi != Epilogue::kInt32;
 
   const Sched sc = make_sched(blockIdx.x, gridDim.x, tiles_m, tiles_n);
   const int nk = K / kBK;                       // stages per tile
@@ -161,9 +190,34 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
                                        (lds_void*)(dst + kBN * kBK + g * kWaves * 1024), 16, 0,
                                        0);
     }
+  };
+  // Loader advance, kept out of the interleaved stage code (it branches).
+  auto advance_loader = [&]() {
     if (++ld_kt == nk) {
       ld_kt = 0;
-      if (++ld_k < sc.count) load_tile(ld_k);
+      if (++ld_k < sc.count) load_tile(ld_k);   // past the end: reloads of the last tile
+    }
+  };
+
+  // Scales of tile k into buffer k % 3: waves 0-3 move 64 weight scales
+  // each, waves 4-7 64 activation scales (one wave-load of one dword per
+  // lane). Tile k + 1's scales go out when tile k starts; the buffer they
+  // overwrite was last read by tile k - 2's epilogue, which every wave
+  // finished before a barrier of tile k - 1.
+  auto issue_scales = [&](int k) {
+    int m0, n0;
+    tile_mn(sc, k, m0, n0);
+    int8_t* buf = scale_bufs + (k % kScaleBufs) * kScaleBytes;
+    if (wave < 4) {
+      int c = n0 + 64 * wave + lane;
+      c = c < N ? c : N - 1;
+      __builtin_amdgcn_global_load_lds((const void*)(w_scale + c), (lds_void*)(buf + wave * 256),
+                                       4, 0, 0);
+    } else {
+      int m = m0 + 64 * (wave - 4) + lane;
+      m = m < M ? m : M - 1;
+      __builtin_amdgcn_global_load_lds((const void*)(a_scale + m),
+                                       (lds_void*)(buf + kBN * 4 + (wave - 4) * 256), 4, 0, 0);
     }
   };
 
@@ -217,11 +271,27 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
       }
     } else {
       uint16_t* o = reinterpret_cast<uint16_t*>(out);
+      // the tile's scales, brought into LDS one tile ahead
+      const uint32_t sbuf = lds_addr(scale_bufs + (k % kScaleBufs) * kScaleBytes);
+      float sa[kTM];
+#pragma unroll
+      for (int j = 0; j < kTM; ++j)
+        sa[j] = lds_read_f1(sbuf + 4 * (kBN + wm * (16 * kTM) + 16 * j + ir));
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {          // two halves of 16 channels
-        float sw[2 * kTN];
-#pragma unroll
-        for (int e = 0; e < 2 * kTN; ++e) sw[e] = w_scale[n_lane + 16 * hf + e];
+        static_assert(2 * kTN == 16, "four vectors of weight scales per half");
+        v4f t0 = lds_read_f4(sbuf + 4 * (wn * 128 + 32 * kq + 16 * hf));
+        v4f t1 = lds_read_f4(sbuf + 4 * (wn * 128 + 32 * kq + 16 * hf + 4));
+        v4f t2 = lds_read_f4(sbuf + 4 * (wn * 128 + 32 * kq + 16 * hf + 8));
+        v4f t3 = lds_read_f4(sbuf + 4 * (wn * 128 + 32 * kq + 16 * hf + 12));
+        // the wait names the loaded registers, so no use moves above it
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(t0), "+v"(t1), "+v"(t2), "+v"(t3), "+v"(sa[0]), "+v"(sa[1]),
+                       "+v"(sa[2]), "+v"(sa[3])
+                     :
+                     : "memory");
+        const float sw[2 * kTN] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3],
+                                   t2[0], t2[1], t2[2], t2[3], t3[0], t3[1], t3[2], t3[3]};
 #pragma unroll
         for (int j = 0; j < kTM; ++j) {
           // Rows past M hold exactly row M-1's sums (their loads were clamped
@@ -229,15 +299,14 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
           // issues its stores and the per-tile store count stays fixed.
           int m = m_lane + 16 * j;
           m = m < M ? m : M - 1;
-          const float sa = a_scale[m];
           uint32_t pk[kTN];
 #pragma unroll
           for (int ii = 0; ii < kTN / 2; ++ii) {
             const int i = (kTN / 2) * hf + ii;
-            const float v0 = ((float)acc[i][j][0] * sa) * sw[4 * ii + 0];
-            const float v1 = ((float)acc[i][j][1] * sa) * sw[4 * ii + 1];
-            const float v2 = ((float)acc[i][j][2] * sa) * sw[4 * ii + 2];
-            const float v3 = ((float)acc[i][j][3] * sa) * sw[4 * ii + 3];
+            const float v0 = ((float)acc[i][j][0] * sa[j]) * sw[4 * ii + 0];
+            const float v1 = ((float)acc[i][j][1] * sa[j]) * sw[4 * ii + 1];
+            const float v2 = ((float)acc[i][j][2] * sa[j]) * sw[4 * ii + 2];
+            const float v3 = ((float)acc[i][j][3] * sa[j]) * sw[4 * ii + 3];
             pk[2 * ii] = pack_bf16x2(v0, v1);
             pk[2 * ii + 1] = pack_bf16x2(v2, v3);
           }
@@ -249,17 +318,22 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
     }
   };
 
-  // Stores of the previous tile's epilogue were issued after the next stage's
-  // loads; the barrier's vmcnt leaves them outstanding. They are counted only
+  // The tile-start group (the previous tile's stores, then the next tile's
+  // scale loads) goes out after the loads of the tile's second stage, so only
+  // the tile's first barrier leaves it outstanding. Stores are counted only
   // when every wave stores a full tile (N a multiple of 256); otherwise the
   // wait covers them too, which is merely slower.
   const int stores_per_tile = (kEpi != Epilogue::kInt32 && N % kBN == 0) ? kStoresPerTile : 0;
   int pending_stores = 0;
 
-  // ---- prologue: stages 0 and 1 in flight; fragments of stage 0, K step 0 ----
-  int issued = 0;
-  for (; issued < kSlots && issued < total; ++issued) issue_next(issued);
-  wait_vmcnt_le(kLoads * (issued - 1));
+  // ---- prologue: tile 0's scales; stages 0 and 1 in flight; fragments of
+  // stage 0, K step 0 ----
+  if constexpr (kScales) issue_scales(0);
+  issue_next(0);
+  advance_loader();
+  issue_next(1);
+  advance_loader();
+  wait_vmcnt_le(kLoads);                 // stage 0 landed
   lds_barrier();
   read_frags(f0, 0, 0);
 
@@ -267,28 +341,55 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   // step 1 from f1; the stage barrier sits between them. --------------------
   int s = 0;
   for (int k = 0; k < sc.count; ++k) {
+    if (kScales && k + 1 < sc.count) {
+      issue_scales(k + 1);
+      pending_stores += kScaleLoads;
+    }
     for (int kt = 0; kt < nk; ++kt, ++s) {
       const int slot = s & 1;
+      // K step 0 (f0), K step 1's fragments read between its MFMAs
       read_frags(f1, slot, 1);
       mfma_all(acc, f0);
-      if (s + 1 < total) {
-        wait_lgkmcnt0();                   // this wave is done reading slot `slot`
-        wait_vmcnt_le(pending_stores);     // stage s+1 has landed
-        lds_barrier();                     // ... for every wave; slot `slot` is free
-        pending_stores = 0;
-        if (issued < total) {
-          issue_next(slot);                // stage s+2 reuses this slot
-          ++issued;
-        }
-        read_frags(f0, slot ^ 1, 0);
+#pragma unroll
+      for (int q = 0; q < kTN + kTM; ++q) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kTN * kTM - (kTN + kTM), 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // Every stage has its barrier and refills a slot, past the last stage
+      // with reloads of a valid stage into slots nothing reads again, so the
+      // code between barriers has no branches and the refill loads and the
+      // next stage's fragment reads interleave with K step 1's MFMAs.
+      wait_lgkmcnt0();                     // this wave is done reading slot `slot`
+      wait_vmcnt_le(pending_stores);       // stage s+1 has landed
+      lds_barrier();                       // ... for every wave; slot `slot` is free
+      __builtin_amdgcn_sched_barrier(0);
+      pending_stores = 0;
+      issue_next(slot);                    // stage s+2 reuses this slot
+      read_frags(f0, slot ^ 1, 0);
       mfma_all(acc, f1);
+#pragma unroll
+      for (int q = 0; q < kLoads; ++q) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < kTN + kTM; ++q) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kTN * kTM - kLoads - (kTN + kTM), 0);
+      __builtin_amdgcn_sched_barrier(0);
+      advance_loader();
     }
     epilogue(k);
     if constexpr (kEpi == Epilogue::kInt32) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     pending_stores = stores_per_tile;
     zero_acc();
   }
+  // LDS DMA still in flight must land before the workgroup's LDS is released.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 }  // namespace pipe
