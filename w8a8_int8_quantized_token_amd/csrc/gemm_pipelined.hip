@@ -12,7 +12,9 @@
 //  * Block tile 256 (n) x 256 (m); each wave owns 128 x 64, held as 8 x 4
 //    v_mfma_i32_16x16x64_i8 accumulators (128 registers).
 //  * K is streamed in 128-byte stages through a 2-slot LDS ring (64 KiB per
-//    slot) filled by global_load_lds_dwordx4 (no register staging).
+//    slot) filled by buffer loads that write LDS directly (no register
+//    staging); a load's address is a descriptor base plus a 32-bit lane
+//    offset plus the stage's K offset in an SGPR.
 //  * Fragments are read one 64-byte K step ahead into a second register set,
 //    so every MFMA finds its operands ready. The single stage barrier sits
 //    between the two K steps of a stage: after it, the next stage's first
@@ -25,8 +27,10 @@
 //  * Weight rows are the MFMA "A" operand with permuted row slots so each
 //    lane ends up with 32 consecutive output channels of one token: the
 //    epilogue writes 64 contiguous bytes per token per lane.
-//  * LDS rows are XOR-swizzled in 16-byte chunks so each 8-lane phase of a
-//    ds_read_b128 touches 8 distinct 16-byte bank groups.
+//  * LDS rows are XOR-swizzled in 16-byte chunks. A ds_read_b128 is served
+//    16 lanes at a time and is conflict-free when those lanes hit 16
+//    distinct 16-byte slots of the 256-byte bank line; the keys below give
+//    every such lane group of the fragment reads distinct slots.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -53,7 +57,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // 128-byte LDS rows hold 8 chunks of 16 bytes; logical chunk c of row r sits
 // at c ^ key(r). Weight rows are read in the permuted slot order (rows r..r+3
-// and r+32..r+35 in one 8-lane phase), activation rows in order.
+// and r+32..r+35 side by side), activation rows in order.
 __device__ __forceinline__ int key_w(int r) { return (r & 3) | (((r >> 5) & 1) << 2); }
 __device__ __forceinline__ int key_a(int r) { return r & 7; }
 
@@ -104,6 +108,25 @@ __device__ __forceinline__ void tile_mn(const Sched& s, int k, int& m0, int& n0)
   const int in = t - g * span;
   m0 = (first + in % gs) * kBM;
   n0 = (in / gs) * kBN;
+}
+
+// Raw buffer resource over [base, base + bytes): the address of a load is an
+// SGPR base plus a 32-bit lane offset plus an SGPR offset, so issuing it costs
+// no 64-bit VALU arithmetic (and anything past the end would read as zero).
+// Word 3 is the gfx9-family raw-buffer descriptor encoding.
+constexpr int kBufferWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferWord3);
+}
+
+// Lane index, recomputed where needed: the empty asm keeps the compiler from
+// merging it with earlier copies, so values derived from it for the tile-level
+// code are not held live across the stage loop.
+__device__ __forceinline__ int lane_id() {
+  int l = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  asm volatile("" : "+v"(l));
+  return l;
 }
 
 // LDS reads of the epilogue's scales. Written as instructions the compiler
@@ -159,36 +182,40 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   const int r_l = 8 * wave + (lane >> 3);
   const int p = lane & 7;
   const int cw = (p ^ key_w(r_l)) << 4, ca = (p ^ key_a(r_l)) << 4;
+  // The tile's weight and activation row blocks as buffers. Rows past N or M
+  // are clamped to the last valid row (their sums duplicate it and are stored
+  // over it with identical values). Lane offsets take two 32-bit operations
+  // per load; a stage adds its K offset in an SGPR.
   int ld_k = 0, ld_kt = 0, ld_rvn = 0, ld_rvm = 0;
-  const int8_t* ld_wb = nullptr;
-  const int8_t* ld_ab = nullptr;
+  __amdgpu_buffer_rsrc_t ld_w, ld_a;
   auto load_tile = [&](int k) {
     int m0, n0;
     tile_mn(sc, k, m0, n0);
-    ld_rvn = ((N - n0) < kBN ? (N - n0) : kBN) - 1;
-    ld_rvm = ((M - m0) < kBM ? (M - m0) : kBM) - 1;
-    ld_wb = w + (int64_t)n0 * ldw;
-    ld_ab = a + (int64_t)m0 * lda;
+    const int rn = (N - n0) < kBN ? (N - n0) : kBN;
+    const int rm = (M - m0) < kBM ? (M - m0) : kBM;
+    ld_rvn = rn - 1;
+    ld_rvm = rm - 1;
+    ld_w = buffer_rsrc(w + (int64_t)n0 * ldw, (uint32_t)(rn * ldw));
+    ld_a = buffer_rsrc(a + (int64_t)m0 * lda, (uint32_t)(rm * lda));
   };
   load_tile(0);
   auto issue_next = [&](int slot) {
-    const int8_t* wb = ld_wb + ld_kt * kBK;
-    const int8_t* ab = ld_ab + ld_kt * kBK;
     int8_t* dst = lds + slot * kSlotBytes + wave * 1024;
+    const int koff = ld_kt * kBK;
 #pragma unroll
     for (int g = 0; g < kLoads / 2; ++g) {
-      int r = r_l + 64 * g;
-      r = r < ld_rvn ? r : ld_rvn;
-      __builtin_amdgcn_global_load_lds((const void*)(wb + (uint32_t)(r * (int)ldw + cw)),
-                                       (lds_void*)(dst + g * kWaves * 1024), 16, 0, 0);
+      const int r = r_l + 64 * g;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_w, (lds_void*)(dst + g * kWaves * 1024), 16,
+                                               (r < ld_rvn ? r : ld_rvn) * (int)ldw + cw, koff,
+                                               0, 0);
     }
 #pragma unroll
     for (int g = 0; g < kLoads / 2; ++g) {
-      int r = r_l + 64 * g;
-      r = r < ld_rvm ? r : ld_rvm;
-      __builtin_amdgcn_global_load_lds((const void*)(ab + (uint32_t)(r * (int)lda + ca)),
-                                       (lds_void*)(dst + kBN * kBK + g * kWaves * 1024), 16, 0,
-                                       0);
+      const int r = r_l + 64 * g;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_a,
+                                               (lds_void*)(dst + kBN * kBK + g * kWaves * 1024),
+                                               16, (r < ld_rvm ? r : ld_rvm) * (int)lda + ca,
+                                               koff, 0, 0);
     }
   };
   // Loader advance, kept out of the interleaved stage code (it branches).
@@ -208,17 +235,17 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
     int m0, n0;
     tile_mn(sc, k, m0, n0);
     int8_t* buf = scale_bufs + (k % kScaleBufs) * kScaleBytes;
-    if (wave < 4) {
-      int c = n0 + 64 * wave + lane;
-      c = c < N ? c : N - 1;
-      __builtin_amdgcn_global_load_lds((const void*)(w_scale + c), (lds_void*)(buf + wave * 256),
-                                       4, 0, 0);
-    } else {
-      int m = m0 + 64 * (wave - 4) + lane;
-      m = m < M ? m : M - 1;
-      __builtin_amdgcn_global_load_lds((const void*)(a_scale + m),
-                                       (lds_void*)(buf + kBN * 4 + (wave - 4) * 256), 4, 0, 0);
-    }
+    // a buffer over the whole scale vector; indices past the end are clamped
+    // to its last element (clamped rows reuse row M-1's scale). The lane
+    // offset is recomputed here rather than kept live across the tile.
+    const int ln = lane_id();
+    const int lim = wave < 4 ? N : M;
+    int idx = (wave < 4 ? n0 + 64 * wave : m0 + 64 * (wave - 4)) + ln;
+    idx = idx < lim ? idx : lim - 1;
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc(wave < 4 ? w_scale : a_scale, (uint32_t)(4 * lim));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + wave * 256), 4, 4 * idx, 0, 0,
+                                             0);
   };
 
   // ---- fragments: MFMA row slot ir = lane % 16 of W tile i maps to wave-local
@@ -251,7 +278,10 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   v4i f0[kTN + kTM], f1[kTN + kTM];
 
   // ---- epilogue of tile k -----------------------------------------------------
+  // ---- epilogue of tile k: lane constants recomputed (not held live) ------
   auto epilogue = [&](int k) {
+    const int el = lane_id();
+    const int ir = el & 15, kq = el >> 4;
     int m0, n0;
     tile_mn(sc, k, m0, n0);
     const int n_wave = n0 + wn * 128;
@@ -262,12 +292,11 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
       int32_t* o = reinterpret_cast<int32_t*>(out);
 #pragma unroll
       for (int j = 0; j < kTM; ++j) {
-        const int m = m_lane + 16 * j;
-        if (m < M) {
-          int32_t* dst = o + (int64_t)m * ldo + n_lane;
+        int m = m_lane + 16 * j;
+        m = m < M ? m : M - 1;      // clamped rows hold row M-1's sums
+        int32_t* dst = o + (int64_t)m * ldo + n_lane;
 #pragma unroll
-          for (int i = 0; i < kTN; ++i) *reinterpret_cast<v4i*>(dst + 4 * i) = acc[i][j];
-        }
+        for (int i = 0; i < kTN; ++i) *reinterpret_cast<v4i*>(dst + 4 * i) = acc[i][j];
       }
     } else {
       uint16_t* o = reinterpret_cast<uint16_t*>(out);
@@ -295,8 +324,9 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
 #pragma unroll
         for (int j = 0; j < kTM; ++j) {
           // Rows past M hold exactly row M-1's sums (their loads were clamped
-          // to it), so they store row M-1's values to row M-1: every lane
-          // issues its stores and the per-tile store count stays fixed.
+          // to it) and its scale, so they store row M-1's values to row M-1:
+          // every lane issues its stores and the per-tile store count stays
+          // fixed.
           int m = m_lane + 16 * j;
           m = m < M ? m : M - 1;
           uint32_t pk[kTN];
