@@ -236,9 +236,13 @@ def test_gemm_postscale(shape, seed):
     ulp_report(bf16_from_dev(out), ref, "postscale vs oracle")
 
 
-@pytest.mark.parametrize("shape,seed", [((64, 128, 256), 61), ((1000, 5120, 5120), 62),
-                                        ((300, 256, 384), 63), ((1, 128, 128), 64),
-                                        ((257, 640, 1024), 65)])
+BLOCKWISE_SHAPES = [((64, 128, 256), 61), ((1000, 5120, 5120), 62), ((300, 256, 384), 63),
+                    ((1, 128, 128), 64), ((257, 640, 1024), 65),
+                    # more tiles than CUs, ragged M, N % 256 == 128
+                    ((8292, 1152, 256), 67), ((4100, 4096, 384), 68), ((129, 384, 13824), 69)]
+
+
+@pytest.mark.parametrize("shape,seed", BLOCKWISE_SHAPES)
 def test_gemm_blockwise(shape, seed):
     M, N, K = shape
     log(f"gemm_blockwise {shape}")
@@ -246,10 +250,34 @@ def test_gemm_blockwise(shape, seed):
     qw = W.random_int8((N, K), seed + 1)
     sa = W.random_scales((M, K // 128), seed + 2)
     sw = W.random_scales((N // 128, K // 128), seed + 3, lo=1e-5, hi=1e-3)
+    if M > 5 and K >= 256:
+        sa[5, 1] = 0.0          # one zero block scale inside a row
+        sa[4, :] = 0.0          # an all-zero row
     out = w8.w8a8_gemm_blockwise(to_dev(qa), to_dev(qw), to_dev(sa), to_dev(sw))
     sync()
     ref = O.gemm_blockwise_bf16(qa, sa, qw, sw)
     ulp_report(bf16_from_dev(out), ref, "blockwise vs oracle")
+
+
+def test_gemm_blockwise_strides_and_guard():
+    log("gemm_blockwise strided operands / guard")
+    M, N, K = 200, 384, 512
+    qa = W.random_int8((M, K), 75)
+    qw = W.random_int8((N, K), 76)
+    sa = W.random_scales((M, K // 128), 77)
+    sw = W.random_scales((N // 128, K // 128), 78, lo=1e-5, hi=1e-3)
+    a_full = torch.zeros((M, K + 256), dtype=torch.int8, device="cuda")
+    a_full[:, :K] = to_dev(qa)
+    w_full = torch.zeros((N, K + 128), dtype=torch.int8, device="cuda")
+    w_full[:, :K] = to_dev(qw)
+    out_full = torch.full((M + 8, N + 64), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    out = out_full[:M, :N]
+    w8.w8a8_gemm_blockwise(a_full[:, :K], w_full[:, :K], to_dev(sa), to_dev(sw), out=out)
+    sync()
+    ref = O.gemm_blockwise_bf16(qa, sa, qw, sw)
+    ulp_report(bf16_from_dev(out), ref, "strided blockwise vs oracle")
+    guard = bf16_from_dev(out_full)
+    assert np.all(guard[M:] == 0xFFFF) and np.all(guard[:M, N:] == 0xFFFF)
 
 
 def test_gemm_guard_rows_and_strides():

@@ -31,8 +31,8 @@
 //    16 lanes at a time and is conflict-free when those lanes hit 16
 //    distinct 16-byte slots of the 256-byte bank line; the keys below give
 //    every such lane group of the fragment reads distinct slots.
-#include "device_common.hpp"
 #include "launch.hpp"
+#include "pipeline.hpp"
 
 namespace w8a8 {
 namespace pipe {
@@ -49,11 +49,6 @@ constexpr int kScaleBytes = (kBN + kBM) * 4;   // one tile's scales
 constexpr int kScaleBufs = 3;                  // tile k's scales sit in buffer k % 3
 constexpr int kScaleLoads = 1;                 // scale wave-loads per wave per tile
 constexpr int kGroupM = 8;
-// Instruction classes of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
-constexpr int kXcds = 8;
-
-typedef __attribute__((address_space(3))) void lds_void;
 
 // 128-byte LDS rows hold 8 chunks of 16 bytes; logical chunk c of row r sits
 // at c ^ key(r). Weight rows are read in the permuted slot order (rows r..r+3
@@ -61,92 +56,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ int key_w(int r) { return (r & 3) | (((r >> 5) & 1) << 2); }
 __device__ __forceinline__ int key_a(int r) { return r & 7; }
 
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// s_waitcnt vmcnt(n) for a run-time n, rounded down (waiting longer is safe).
-__device__ __forceinline__ void wait_vmcnt_le(int n) {
-  if (n >= 17) asm volatile("s_waitcnt vmcnt(17)" ::: "memory");
-  else if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if (n >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if (n >= 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
-// This workgroup's tiles: logical ids start + k * stride, k < count.
-struct Sched {
-  int start, stride, count, tiles_m, tiles_n;
-};
-
-__device__ __forceinline__ Sched make_sched(int b, int grid, int tiles_m, int tiles_n) {
-  Sched s;
-  s.tiles_m = tiles_m;
-  s.tiles_n = tiles_n;
-  const int T = tiles_m * tiles_n;
-  const int x = b % kXcds, j = b / kXcds;
-  const int nwg = grid / kXcds + (x < grid % kXcds ? 1 : 0);     // workgroups on XCD x
-  const int tx = T / kXcds + (x < T % kXcds ? 1 : 0);            // tiles of XCD x
-  const int sx = x * (T / kXcds) + (x < T % kXcds ? x : T % kXcds);
-  s.start = sx + j;
-  s.stride = nwg;
-  s.count = j < tx ? (tx - j + nwg - 1) / nwg : 0;
-  return s;
-}
-
-// M-grouped order: groups of kGroupM tile rows, n fastest within a group.
 __device__ __forceinline__ void tile_mn(const Sched& s, int k, int& m0, int& n0) {
-  const int t = s.start + k * s.stride;
-  const int span = kGroupM * s.tiles_n;
-  const int g = t / span;
-  const int first = g * kGroupM;
-  const int gs = (s.tiles_m - first) < kGroupM ? (s.tiles_m - first) : kGroupM;
-  const int in = t - g * span;
-  m0 = (first + in % gs) * kBM;
-  n0 = (in / gs) * kBN;
-}
-
-// Raw buffer resource over [base, base + bytes): the address of a load is an
-// SGPR base plus a 32-bit lane offset plus an SGPR offset, so issuing it costs
-// no 64-bit VALU arithmetic (and anything past the end would read as zero).
-// Word 3 is the gfx9-family raw-buffer descriptor encoding.
-constexpr int kBufferWord3 = 0x00020000;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           kBufferWord3);
-}
-
-// Lane index, recomputed where needed: the empty asm keeps the compiler from
-// merging it with earlier copies, so values derived from it for the tile-level
-// code are not held live across the stage loop.
-__device__ __forceinline__ int lane_id() {
-  int l = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-  asm volatile("" : "+v"(l));
-  return l;
-}
-
-// LDS reads of the epilogue's scales. Written as instructions the compiler
-// does not analyse: otherwise it cannot tell them apart from the LDS targets
-// of the loads still in flight (global_load_lds) and waits for all of those
-// first, draining the pipeline at every tile. The data they read is
-// published by the stage barriers, and the caller waits for the reads.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-typedef float v4f __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ v4f lds_read_f4(uint32_t addr) {
-  v4f v;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
-  return v;
-}
-__device__ __forceinline__ float lds_read_f1(uint32_t addr) {
-  float v;
-  asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr) : "memory");
-  return v;
+  tile_mn<kBM, kBN, kGroupM>(s, k, m0, n0);
 }
 
 __device__ __forceinline__ void mfma_all(v4i (&acc)[kTN][kTM], const v4i (&f)[kTN + kTM]) {
@@ -424,7 +335,7 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
 
 }  // namespace pipe
 
-static int cu_count() {
+int device_cu_count() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -444,7 +355,8 @@ hipError_t launch_gemm_pipelined(Epilogue epi, const int8_t* a, int64_t lda, con
   const int tiles_m = (int)((M + pipe::kBM - 1) / pipe::kBM);
   const int tiles_n = (int)((N + pipe::kBN - 1) / pipe::kBN);
   const int64_t tiles = (int64_t)tiles_m * tiles_n;
-  const int grid = (int)(tiles < cu_count() ? tiles : cu_count());
+  const int cus = device_cu_count();
+  const int grid = (int)(tiles < cus ? tiles : cus);
   const dim3 block(pipe::kThreads);
   if (epi == Epilogue::kInt32)
     hipLaunchKernelGGL((pipe::gemm_i8_pipelined<Epilogue::kInt32>), dim3(grid), block, 0, st, a,

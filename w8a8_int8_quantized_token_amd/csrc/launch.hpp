@@ -20,11 +20,20 @@ hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float 
 
 enum class Epilogue { kPostscaleBf16, kInt32, kBlockwiseBf16 };
 
+// Compute units of the current device (cached per device); persistent grids
+// launch at most one workgroup per CU.
+int device_cu_count();
+
 // Persistent pipelined kernel (post-scale and INT32 epilogues).
 hipError_t launch_gemm_pipelined(Epilogue epi, const int8_t* a, int64_t lda, const int8_t* w,
                                  int64_t ldw, const float* a_scale, const float* w_scale,
                                  void* out, int64_t ldo, int64_t M, int64_t N, int64_t K,
                                  hipStream_t st);
+
+// Persistent pipelined kernel with per-K-block scales.
+hipError_t launch_gemm_blockwise(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
+                                 const float* a_scale, const float* w_scale, uint16_t* out,
+                                 int64_t ldo, int64_t M, int64_t N, int64_t K, hipStream_t st);
 
 hipError_t launch_gemm(Epilogue epi, const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
                        const float* a_scale, const float* w_scale, void* out, int64_t ldo,
