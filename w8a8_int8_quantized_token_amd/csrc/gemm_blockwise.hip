@@ -14,17 +14,17 @@
 //    v_mfma_i32_16x16x64_i8 accumulators (64 registers) plus 64 fp32 running
 //    sums, which leaves room for two fragment sets at two waves per SIMD.
 //  * One pipeline stage is one 128-wide K block: 48 KiB of codes plus the
-//    block's scales, moved into a 2-slot LDS ring by buffer loads that write
+//    block's scales, moved into a 3-slot LDS ring by buffer loads that write
 //    LDS directly. Every wave issues the same seven loads per stage (waves 0
 //    and 1 bring the 128 activation scales, the others the two weight
 //    scales), so each wave's vmcnt bookkeeping is the same.
-//  * The rescale (a convert and an FMA per output per block) is the VALU work
-//    of this kernel, as much as the MFMA time at two waves per SIMD. It is
-//    split over the two K steps: the first half of the tiles is rescaled
-//    after their second-K-step MFMAs in the block's own stage, the second
-//    half at the start of the next stage, just before their accumulators are
-//    restarted at zero. Each half sits between MFMAs, so one wave's rescale
-//    overlaps the other wave's MFMAs on the same SIMD.
+//  * The rescale (a convert and an FMA per output per block: 128 VALU
+//    instructions per wave per stage against 32 MFMAs) is this kernel's
+//    VALU work. On gfx950 VALU instructions hide only partly behind MFMAs,
+//    so it is spread thinly: the first half of the tiles is rescaled between
+//    the second-K-step MFMAs of the block's own stage, the second half
+//    between the first-K-step MFMAs of the next stage, just before those
+//    accumulators restart at zero.
 //  * Grid, tile order, LDS swizzle and row clamping follow the post-scale
 //    kernel: persistent, XCD-aware, M-grouped; rows past N or M load (and
 //    store) the last valid row.
@@ -43,11 +43,13 @@ constexpr int kHalf = kTN / 2;        // tiles i < kHalf are rescaled in their o
 constexpr int kTileBytes = (kBN + kBM) * kBK;          // 48 KiB of codes per stage
 constexpr int kScaleArea = kWaves * 256;               // one dword wave-load per wave
 constexpr int kSlotBytes = kTileBytes + kScaleArea;
-constexpr int kSlots = 2;
 constexpr int kLoads = kTileBytes / 1024 / kWaves;     // 1 KiB code wave-loads per wave: 6
 constexpr int kStageLoads = kLoads + 1;                // plus the scale wave-load
 constexpr int kStoresPerTile = kTM * 2;                // 16-byte stores per wave per tile
 constexpr int kGroupM = 8;
+// Three slots (150 KiB of LDS) keep two stages in flight behind the one being
+// consumed; two slots also work and measured about 4% slower.
+constexpr int kRingSlots = 3;
 static_assert(kLoads == kBN / 64 + kBM / 64, "code rows split evenly over the waves");
 
 // Swizzle keys of the 128-byte LDS rows (logical 16-byte chunk c of row r at
@@ -56,6 +58,7 @@ static_assert(kLoads == kBN / 64 + kBM / 64, "code rows split evenly over the wa
 __device__ __forceinline__ int key_w(int r) { return (r & 3) | (((r >> 4) & 1) << 2); }
 __device__ __forceinline__ int key_a(int r) { return r & 7; }
 
+template <int kSlots>
 __global__ __launch_bounds__(kThreads, 1)
 void gemm_i8_blockwise(const int8_t* __restrict__ a, int64_t lda, const int8_t* __restrict__ w,
                        int64_t ldw, const float* __restrict__ a_scale,
@@ -212,19 +215,21 @@ void gemm_i8_blockwise(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   const int stores_per_tile = (N % kBN == 0) ? kStoresPerTile : 0;
   int pending_stores = 0;
 
-  // ---- prologue: stages 0 and 1 in flight; stage 0's K step 0 fragments ----
-  issue_next(0);
-  advance_loader();
-  issue_next(1);
-  advance_loader();
-  wait_vmcnt_le(kStageLoads);            // stage 0 landed
+  // ---- prologue: the first kSlots stages in flight; stage 0's K step 0
+  // fragments ----
+#pragma unroll
+  for (int i = 0; i < kSlots; ++i) {
+    issue_next(i);
+    advance_loader();
+  }
+  wait_vmcnt_le(kStageLoads * (kSlots - 1));   // stage 0 landed
   lds_barrier();
   read_frags(f0, 0, 0);
 
-  int s = 0;
+  int slot = 0;
   for (int k = 0; k < sc.count; ++k) {
-    for (int kt = 0; kt < nk; ++kt, ++s) {
-      const int slot = s & 1;
+    for (int kt = 0; kt < nk; ++kt) {
+      const int next = slot + 1 == kSlots ? 0 : slot + 1;
       const uint32_t sl = lds0 + slot * kSlotBytes;
       // ---- K step 0: accumulators restart at zero; the previous block's
       // second-half rescale goes first, tile by tile, between the MFMAs.
@@ -261,7 +266,9 @@ void gemm_i8_blockwise(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
                    : "+v"(sa[0]), "+v"(sa[1]), "+v"(sa[2]), "+v"(sa[3]), "+v"(swv)
                    :
                    : "memory");
-      wait_vmcnt_le(pending_stores);
+      // (the loads of the kSlots - 2 stages after it and the previous tile's
+      // stores may still be in flight)
+      wait_vmcnt_le(kStageLoads * (kSlots - 2) + pending_stores);
       lds_barrier();                       // ... for every wave; slot `slot` is free
       __builtin_amdgcn_sched_barrier(0);
       pending_stores = 0;
@@ -270,8 +277,8 @@ void gemm_i8_blockwise(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
       for (int j = 0; j < kTM; ++j) s_cur[j] = sa[j] * swv;
       // ---- K step 1, the refill of this slot, the next stage's first
       // fragments, and this block's first-half rescale after its MFMAs.
-      issue_next(slot);
-      read_frags(f0, slot ^ 1, 0);
+      issue_next(slot);                    // stage s + kSlots
+      read_frags(f0, next, 0);
 #pragma unroll
       for (int i = 0; i < kTN; ++i)
 #pragma unroll
@@ -297,6 +304,7 @@ void gemm_i8_blockwise(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
       advance_loader();
 #pragma unroll
       for (int j = 0; j < kTM; ++j) s_prev[j] = s_cur[j];
+      slot = next;
     }
     // the tile's last block: second-half rescale, then the output
 #pragma unroll
@@ -329,7 +337,7 @@ hipError_t launch_gemm_blockwise(const int8_t* a, int64_t lda, const int8_t* w, 
   const int64_t tiles = (int64_t)tiles_m * tiles_n;
   const int cus = device_cu_count();
   const int grid = (int)(tiles < cus ? tiles : cus);
-  hipLaunchKernelGGL(pipe::bw::gemm_i8_blockwise, dim3(grid), dim3(pipe::bw::kThreads), 0, st, a,
+  hipLaunchKernelGGL(pipe::bw::gemm_i8_blockwise<pipe::bw::kRingSlots>, dim3(grid), dim3(pipe::bw::kThreads), 0, st, a,
                      lda, w, ldw, a_scale, w_scale, out, ldo, (int)M, (int)N, (int)K, tiles_m,
                      tiles_n);
   return hipGetLastError();

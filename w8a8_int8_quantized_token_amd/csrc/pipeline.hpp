@@ -29,6 +29,8 @@ __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcn
 __device__ __forceinline__ void wait_vmcnt_le(int n) {
   if (n >= 17) asm volatile("s_waitcnt vmcnt(17)" ::: "memory");
   else if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (n >= 15) asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+  else if (n >= 14) asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
   else if (n >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   else if (n >= 7) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
   else if (n >= 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
