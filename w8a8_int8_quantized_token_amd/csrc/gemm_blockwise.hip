@@ -127,6 +127,9 @@ void gemm_i8_blockwise(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
         ld_s, (lds_void*)(lds + slot * kSlotBytes + kTileBytes + wave * 256), 4, ld_vs,
         ld_kt * 4, 0, 0);
   };
+  // Loader advance. It branches, so it runs at the top of a stage: placed after
+  // the stage's code it would give the compiler a block past the branch into
+  // which it sinks work meant to hide behind the stage's MFMAs.
   auto advance_loader = [&]() {
     if (++ld_kt == nk) {
       ld_kt = 0;
@@ -219,8 +222,8 @@ void gemm_i8_blockwise(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   // fragments ----
 #pragma unroll
   for (int i = 0; i < kSlots; ++i) {
+    if (i > 0) advance_loader();
     issue_next(i);
-    advance_loader();
   }
   wait_vmcnt_le(kStageLoads * (kSlots - 1));   // stage 0 landed
   lds_barrier();
@@ -231,6 +234,7 @@ void gemm_i8_blockwise(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
     for (int kt = 0; kt < nk; ++kt) {
       const int next = slot + 1 == kSlots ? 0 : slot + 1;
       const uint32_t sl = lds0 + slot * kSlotBytes;
+      advance_loader();                    // to stage s + kSlots
       // ---- K step 0: accumulators restart at zero; the previous block's
       // second-half rescale goes first, tile by tile, between the MFMAs.
       float sa[kTM], swv;
@@ -301,7 +305,6 @@ void gemm_i8_blockwise(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      advance_loader();
 #pragma unroll
       for (int j = 0; j < kTM; ++j) s_prev[j] = s_cur[j];
       slot = next;

@@ -129,7 +129,10 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
                                                koff, 0, 0);
     }
   };
-  // Loader advance, kept out of the interleaved stage code (it branches).
+  // Loader advance. It branches, so it runs at the top of a stage: placed after
+  // the stage's code it would give the compiler a block past the branch into
+  // which it sinks the next stage's fragment reads, away from the MFMAs they
+  // should hide behind.
   auto advance_loader = [&]() {
     if (++ld_kt == nk) {
       ld_kt = 0;
@@ -273,7 +276,6 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   issue_next(0);
   advance_loader();
   issue_next(1);
-  advance_loader();
   wait_vmcnt_le(kLoads);                 // stage 0 landed
   lds_barrier();
   read_frags(f0, 0, 0);
@@ -288,6 +290,7 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
     }
     for (int kt = 0; kt < nk; ++kt, ++s) {
       const int slot = s & 1;
+      advance_loader();                    // to stage s+2
       // K step 0 (f0), K step 1's fragments read between its MFMAs
       read_frags(f1, slot, 1);
       mfma_all(acc, f0);
@@ -322,7 +325,6 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
       }
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, kTN * kTM - kLoads - (kTN + kTM), 0);
       __builtin_amdgcn_sched_barrier(0);
-      advance_loader();
     }
     epilogue(k);
     if constexpr (kEpi == Epilogue::kInt32) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
