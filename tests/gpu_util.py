@@ -31,3 +31,17 @@ def from_dev(t: torch.Tensor) -> np.ndarray:
 
 def log(msg: str) -> None:
     print(msg, flush=True)
+
+
+def check_inv_rms(r_gpu: np.ndarray, r_ref: np.ndarray, cols: int) -> float:
+    """RMSNorm's r: the order of its reduction is not fixed, so the device value
+    must lie within (ceil(log2 K) + 4) * 2^-24 * r of the oracle's (which sums
+    exact squares in fp64 and rounds once). Returns the largest error seen, in
+    units of 2^-24 * r."""
+    r_gpu = np.asarray(r_gpu, np.float64)
+    r_ref = np.asarray(r_ref, np.float64)
+    bound = (int(np.ceil(np.log2(cols))) + 4) * 2.0 ** -24
+    rel = np.abs(r_gpu - r_ref) / np.where(r_ref > 0, r_ref, 1.0)
+    assert np.all(np.isfinite(r_gpu)) and np.all(rel <= bound), \
+        f"inv_rms off by {rel.max() / 2.0 ** -24:.2f} x 2^-24 (bound {bound / 2.0 ** -24:.0f})"
+    return float(rel.max() / 2.0 ** -24)

@@ -4,8 +4,8 @@ Bars: INT8 codes, fp32 scales and INT32 accumulators bit-exact; BF16 outputs
 within 1 BF16 ulp (the kernels perform the same fp32 operations in the same
 order as the oracle, so the count of 1-ulp differences is also reported and
 expected to be 0). RMSNorm's r (an fp32 reduction whose order is not fixed)
-must be within 1 fp32 ulp of the oracle's, and everything downstream of r is
-compared bit for bit given the device's r.
+must be within (ceil(log2 K) + 4) * 2^-24 * r of the oracle's, and everything
+downstream of r is compared bit for bit given the device's r.
 """
 from __future__ import annotations
 
@@ -16,7 +16,7 @@ import torch
 import oracle as O
 import workloads as W
 import w8a8_int8_quantized_token_amd as w8
-from tests.gpu_util import bf16_from_dev, bf16_to_dev, from_dev, log, to_dev
+from tests.gpu_util import bf16_from_dev, bf16_to_dev, check_inv_rms, from_dev, log, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -153,8 +153,9 @@ def test_quant_exhaustive_bf16_pairs():
 
 
 def test_rmsnorm_quant():
+    # full rows of 1, 4 and 8 vectors per lane, few and many rows
     for shape, seed in (((64, 256), 31), ((2048, 4096), 32), ((100, 13824), 33), ((5, 16384), 34),
-                        ((3, 8), 35)):
+                        ((3, 8), 35), ((777, 2048), 36), ((3, 512), 37), ((40000, 512), 38)):
         log(f"rmsnorm_quant {shape}")
         x = W.random_bits(shape, seed)
         if shape[0] >= 8:
@@ -162,16 +163,17 @@ def test_rmsnorm_quant():
             x[1] = 0x4040                                             # constant 3.0
             x[2] = W.random_bits((shape[1],), seed + 1, std=1e-3)     # eps matters
             x[3] = W.random_bits((shape[1],), seed + 2, std=300.0)
+            x[4] = W.random_bits((shape[1],), seed + 4, std=1e25)     # squares overflow fp32
+            x[5] = W.random_bits((shape[1],), seed + 5, std=1e-22)    # squares below fp32 normals
         g = W.random_bits((shape[1],), seed + 3, std=0.1, mean=1.0)
-        for gamma in (g, np.zeros_like(g)):
-            q, s, r = w8.w8a8_rmsnorm_quant(bf16_to_dev(x), bf16_to_dev(gamma), 1e-6)
+        for gamma, eps in ((g, 1e-6), (np.zeros_like(g), 1e-6), (g, 0.0)):
+            xs = x if eps > 0 else x[1:]                              # eps 0: no all-zero row
+            q, s, r = w8.w8a8_rmsnorm_quant(bf16_to_dev(xs), bf16_to_dev(gamma), eps)
             sync()
             rg = from_dev(r)
-            rref = O.rmsnorm_inv_rms(x, 1e-6)
-            ulp = np.abs(rg.view(np.int32).astype(np.int64) - rref.view(np.int32).astype(np.int64))
-            assert ulp.max() <= 1, f"inv_rms off by {ulp.max()} ulp"
-            log(f"  inv_rms exact in {np.mean(ulp == 0):.6f} of rows")
-            qo, so, _ = O.rmsnorm_quant(x, gamma, 1e-6, r=rg)
+            err = check_inv_rms(rg, O.rmsnorm_inv_rms(xs, eps), shape[1])
+            log(f"  eps {eps}: inv_rms max error {err:.2f} x 2^-24 r")
+            qo, so, _ = O.rmsnorm_quant(xs, gamma, eps, r=rg)
             assert np.array_equal(from_dev(q), qo)
             assert np.array_equal(from_dev(s).view(np.uint32), so.view(np.uint32))
 

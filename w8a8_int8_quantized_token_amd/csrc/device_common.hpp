@@ -36,24 +36,60 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Wave reductions (64 lanes)
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t o = __shfl_xor(v, off, kWave);
-    v = v > o ? v : o;
-  }
-  return v;
+// Within each 16-lane row, DPP moves (no LDS round trip): two quad swaps
+// (lane ^ 1, lane ^ 2), then rotations of the row by 4 and 8 lanes. After
+// the four steps every lane of a row holds an op over the whole row; the
+// rows are then combined from lanes 0, 16, 32 and 48 with v_readlane.
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, 0xF, 0xF, false);
 }
 
-// Max over aligned groups of `width` lanes (width a power of two <= 64).
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// Max over each 16-lane row, in every lane of the row.
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+  v = umax(v, dpp_u32<kDppQuadXor1>(v));
+  v = umax(v, dpp_u32<kDppQuadXor2>(v));
+  v = umax(v, dpp_u32<kDppRowRor4>(v));
+  return umax(v, dpp_u32<kDppRowRor8>(v));
+}
+
+// Max over the wave (uniform result).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = row_max_u32(v);
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return umax(umax(a, b), umax(c, d));
+}
+
+// Max over aligned groups of 16 lanes (one DPP row), in every lane.
 template <int kWidth>
 __device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = kWidth / 2; off >= 1; off >>= 1) {
-    uint32_t o = __shfl_xor(v, off, kWave);
-    v = v > o ? v : o;
-  }
-  return v;
+  static_assert(kWidth == 16, "groups are DPP rows");
+  return row_max_u32(v);
+}
+
+// Pairwise fp32 sum over the wave (uniform result): depth 4 within a row,
+// then (row 0 + row 1) + (row 2 + row 3) from one lane of each row.
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  uint32_t v = __float_as_uint(x);
+  v = __float_as_uint(__uint_as_float(v) + __uint_as_float(dpp_u32<kDppQuadXor1>(v)));
+  v = __float_as_uint(__uint_as_float(v) + __uint_as_float(dpp_u32<kDppQuadXor2>(v)));
+  v = __float_as_uint(__uint_as_float(v) + __uint_as_float(dpp_u32<kDppRowRor4>(v)));
+  v = __float_as_uint(__uint_as_float(v) + __uint_as_float(dpp_u32<kDppRowRor8>(v)));
+  const float a = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)v, 0));
+  const float b = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const float c = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)v, 32));
+  const float d = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return (a + b) + (c + d);
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
@@ -108,9 +144,9 @@ __device__ __forceinline__ float quant_quotient(float x, const QuantParams& p) {
   }
 }
 
-// Low byte of the result is the INT8 code.
+// Low byte of the result is the INT8 code (the clamp is one v_med3_f32).
 __device__ __forceinline__ uint32_t quant_code_bits(float t) {
-  t = __builtin_fminf(__builtin_fmaxf(t, -127.0f), 127.0f);
+  t = __builtin_amdgcn_fmed3f(t, -127.0f, 127.0f);
   return __float_as_uint(t + 12582912.0f);   // 1.5 * 2^23
 }
 

@@ -29,11 +29,26 @@ __device__ __forceinline__ U4 load_nt(const U4* p) {
   return v;
 }
 
+// Absolute maxima kept as two 16-bit lanes (low and high BF16 of each pair):
+// the magnitude bits of non-negative BF16 order like the values, so a packed
+// unsigned 16-bit max (v_pk_max_u16) takes two maxima per instruction.
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t absmax2_u4(const U4& v, uint32_t m2) {
+  const v2u16 a = __builtin_bit_cast(v2u16, v.x & 0x7FFF7FFFu);
+  const v2u16 b = __builtin_bit_cast(v2u16, v.y & 0x7FFF7FFFu);
+  const v2u16 c = __builtin_bit_cast(v2u16, v.z & 0x7FFF7FFFu);
+  const v2u16 d = __builtin_bit_cast(v2u16, v.w & 0x7FFF7FFFu);
+  const v2u16 t = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                            __builtin_elementwise_max(c, d));
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(t, __builtin_bit_cast(v2u16, m2)));
+}
+__device__ __forceinline__ uint32_t fold_absmax(uint32_t m2) {
+  const uint32_t lo = m2 & 0xFFFFu, hi = m2 >> 16;
+  return lo > hi ? lo : hi;
+}
 __device__ __forceinline__ uint32_t absmax_u4(const U4& v, uint32_t m) {
-  m = absmax_bits_bf16x2(v.x, m);
-  m = absmax_bits_bf16x2(v.y, m);
-  m = absmax_bits_bf16x2(v.z, m);
-  return absmax_bits_bf16x2(v.w, m);
+  const uint32_t r = fold_absmax(absmax2_u4(v, 0u));
+  return r > m ? r : m;
 }
 
 // Eight BF16 -> eight INT8 codes (two dwords).
@@ -107,10 +122,10 @@ void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t col
   load_row<kVpl, kFull>(v, xr, lane, nvec);
   uint2* qr = reinterpret_cast<uint2*>(q + row * ldq);
   if constexpr (!kGroup128) {
-    uint32_t m = 0;
+    uint32_t m2 = 0;
 #pragma unroll
-    for (int j = 0; j < kVpl; ++j) m = absmax_u4(v[j], m);
-    m = wave_max_u32(m);
+    for (int j = 0; j < kVpl; ++j) m2 = absmax2_u4(v[j], m2);
+    const uint32_t m = wave_max_u32(fold_absmax(m2));
     const QuantParams p = quant_params(bf16_bits_to_float(m));
     if (p.fast) store_row_codes<kVpl, kFull, true>(v, qr, lane, nvec, p);
     else store_row_codes<kVpl, kFull, false>(v, qr, lane, nvec, p);
@@ -214,8 +229,36 @@ void quant_block128_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t
 //   r = fl32(1 / sqrt(sum(x^2) / K + eps)), the sum of exact squares in fp64;
 //   y = bf16(fl32(fl32(x * r) * gamma)); codes and scale from y.
 // ---------------------------------------------------------------------------
+// Sum of the eight exact squares of a vector in fp32: each v_dot2 adds two
+// BF16 squares (exact products), then a pairwise tree.
+__device__ __forceinline__ float sumsq8_f32(const U4& v) {
+  const auto bf = [](uint32_t d) { return __builtin_bit_cast(v2bf, d); };
+  const float a = __builtin_amdgcn_fdot2_f32_bf16(bf(v.x), bf(v.x), 0.0f, false);
+  const float b = __builtin_amdgcn_fdot2_f32_bf16(bf(v.y), bf(v.y), 0.0f, false);
+  const float c = __builtin_amdgcn_fdot2_f32_bf16(bf(v.z), bf(v.z), 0.0f, false);
+  const float d = __builtin_amdgcn_fdot2_f32_bf16(bf(v.w), bf(v.w), 0.0f, false);
+  return (a + b) + (c + d);
+}
+
+// Pairwise sum of t[lo, hi).
+template <int kLo, int kHi>
+__device__ __forceinline__ float tree_sum(const float* t) {
+  if constexpr (kHi - kLo == 1) {
+    return t[kLo];
+  } else {
+    constexpr int kMid = kLo + (kHi - kLo) / 2;
+    return tree_sum<kLo, kMid>(t) + tree_sum<kMid, kHi>(t);
+  }
+}
+
+// fp64 sum of exact squares, for rows whose fp32 sum leaves the safe range.
+// The words pass through an empty asm so the compiler cannot share their
+// BF16 -> fp32 unpacking with the normalisation that follows: sharing hoists
+// the unpacking above this rarely taken branch and keeps 64 unpacked floats
+// live for the whole row.
 __device__ __forceinline__ double sumsq_u4(const U4& v, double acc) {
-  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  asm volatile("" : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3]));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const double a = (double)bf16_lo(d[i]);
@@ -240,6 +283,77 @@ __device__ __forceinline__ U4 rmsnorm_u4(const U4& v, const U4& g, float r) {
   return U4{o[0], o[1], o[2], o[3]};
 }
 
+// One row: r from the sum of squares, y = bf16(x r g) in place, absmax,
+// codes and the row's scale (and r) written out.
+template <int kVpl, bool kFull, int kChunk>
+__device__ __forceinline__ void rmsnorm_quant_row(U4 (&v)[kVpl], const U4* g, const U4* gr,
+                                                  int lane, int nvec, int64_t cols, float eps,
+                                                  uint2* qr, float* scale_out,
+                                                  float* inv_rms_out) {
+  // Sum of squares in fp32, pairwise from the squares up (depth about
+  // log2(cols) + 2, all terms non-negative): relative error at most about
+  // (log2(cols) + 4) * 2^-24, so r is within half that plus one rounding of
+  // the fp64 reference. Rows whose fp32 sum is huge (squares may overflow)
+  // or tiny (squares may be subnormal) take an fp64 sum instead; the choice
+  // is uniform over the wave.
+  float part[kVpl];
+#pragma unroll
+  for (int j = 0; j < kVpl; ++j) part[j] = sumsq8_f32(v[j]);
+  const float ss32 = wave_sum_f32(tree_sum<0, kVpl>(part));
+  double ss;
+  if (ss32 >= 0x1p-80f && ss32 <= 0x1p100f) {
+    ss = (double)ss32;
+  } else {
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < kVpl; ++j) acc = sumsq_u4(v[j], acc);
+    ss = wave_sum_f64(acc);
+  }
+  const double r64 = 1.0 / __builtin_sqrt(ss / (double)cols + (double)eps);
+  const float r = (float)r64;
+  // Gains: g holds all kVpl vectors (kChunk == kVpl), or null and they are
+  // fetched from gr in chunks of kChunk.
+  uint32_t m2 = 0;
+#pragma unroll
+  for (int j0 = 0; j0 < kVpl; j0 += kChunk) {
+    U4 gc[kChunk];
+#pragma unroll
+    for (int jj = 0; jj < kChunk; ++jj) {
+      const int j = j0 + jj;
+      if (j < kVpl) {
+        if constexpr (kChunk == kVpl) {
+          // through an empty asm: in a loop over rows the compiler would
+          // otherwise hoist the unpacking of these loop-invariant words and
+          // hold 64 unpacked floats instead of 32 packed ones
+          U4 t = g[j];
+          asm volatile("" : "+v"(t.x), "+v"(t.y), "+v"(t.z), "+v"(t.w));
+          gc[jj] = t;
+        } else {
+          const int idx = lane + j * kWave;
+          gc[jj] = gr[kFull || idx < nvec ? idx : nvec - 1];
+        }
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < kChunk && j0 + jj < kVpl; ++jj) {
+      const int j = j0 + jj;
+      v[j] = rmsnorm_u4(v[j], gc[jj], r);   // padding: x = 0 gives y = 0
+      m2 = absmax2_u4(v[j], m2);
+    }
+  }
+  const uint32_t m = wave_max_u32(fold_absmax(m2));
+  const QuantParams p = quant_params(bf16_bits_to_float(m));
+  if (p.fast) store_row_codes<kVpl, kFull, true>(v, qr, lane, nvec, p);
+  else store_row_codes<kVpl, kFull, false>(v, qr, lane, nvec, p);
+  if (lane == 0) {
+    *scale_out = p.s;
+    if (inv_rms_out) *inv_rms_out = r;
+  }
+}
+
+// One wave per row. Short rows load the gains up front; long rows (over 16
+// vectors per lane) fetch them in chunks after the reduction to stay within
+// the register budget.
 template <int kVpl, bool kFull>
 __global__ __launch_bounds__(kRowsPerBlock * kWave)
 void rmsnorm_quant_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
@@ -250,49 +364,15 @@ void rmsnorm_quant_kernel(const uint16_t* __restrict__ x, const uint16_t* __rest
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int nvec = (int)(cols >> 3);
-  const U4* xr = reinterpret_cast<const U4*>(x + row * ldx);
   const U4* gr = reinterpret_cast<const U4*>(gamma);
-  // The row is streamed from HBM; the gains are L2-resident. Short rows load
-  // both up front; long rows (over 16 vectors per lane) fetch the gains in
-  // chunks after the reduction to stay within the register budget.
   constexpr bool kGainsEarly = kVpl <= 16;
-  constexpr int kChunk = kGainsEarly ? kVpl : 8;
   U4 v[kVpl];
-  U4 g[kGainsEarly ? kVpl : kChunk];
-  load_row<kVpl, kFull>(v, xr, lane, nvec);
+  U4 g[kGainsEarly ? kVpl : 1];
+  load_row<kVpl, kFull>(v, reinterpret_cast<const U4*>(x + row * ldx), lane, nvec);
   if constexpr (kGainsEarly) load_row<kVpl, kFull, false>(g, gr, lane, nvec);
-  double ss = 0.0;
-#pragma unroll
-  for (int j = 0; j < kVpl; ++j) ss = sumsq_u4(v[j], ss);
-  ss = wave_sum_f64(ss);
-  const double r64 = 1.0 / __builtin_sqrt(ss / (double)cols + (double)eps);
-  const float r = (float)r64;
-  uint32_t m = 0;
-#pragma unroll
-  for (int j0 = 0; j0 < kVpl; j0 += kChunk) {
-    if constexpr (!kGainsEarly) {
-#pragma unroll
-      for (int jj = 0; jj < kChunk; ++jj) {
-        const int idx = lane + (j0 + jj) * kWave;
-        if (j0 + jj < kVpl) g[jj] = gr[kFull || idx < nvec ? idx : nvec - 1];
-      }
-    }
-#pragma unroll
-    for (int jj = 0; jj < kChunk && j0 + jj < kVpl; ++jj) {
-      const int j = j0 + jj;
-      v[j] = rmsnorm_u4(v[j], g[kGainsEarly ? j : jj], r);   // padding: x = 0 gives y = 0
-      m = absmax_u4(v[j], m);
-    }
-  }
-  m = wave_max_u32(m);
-  const QuantParams p = quant_params(bf16_bits_to_float(m));
-  uint2* qr = reinterpret_cast<uint2*>(q + row * ldq);
-  if (p.fast) store_row_codes<kVpl, kFull, true>(v, qr, lane, nvec, p);
-  else store_row_codes<kVpl, kFull, false>(v, qr, lane, nvec, p);
-  if (lane == 0) {
-    scale[row] = p.s;
-    if (inv_rms) inv_rms[row] = r;
-  }
+  rmsnorm_quant_row<kVpl, kFull, kGainsEarly ? kVpl : 8>(
+      v, g, gr, lane, nvec, cols, eps, reinterpret_cast<uint2*>(q + row * ldq), scale + row,
+      inv_rms ? inv_rms + row : nullptr);
 }
 
 template <int kVpl, bool kFull>
