@@ -44,7 +44,9 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    # about 0.2 s of untimed steps at the default workload: the engine clock
+    # needs ~150 ms of load to ramp before timing is representative
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="up_proj")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-bf16", action="store_true", help="skip the torch BF16 Linear yardstick")

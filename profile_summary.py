@@ -3,8 +3,9 @@
 Called as ``python bench.py --summarize PROF_DIR``. PROF_DIR holds the
 outputs of these commands (run from the repository root, TMPDIR=/tmp):
 
+  rocprofv3 --kernel-trace --stats -d PROF_DIR/kt_up_proj -o kt -- python3 bench.py
   rocprofv3 --kernel-trace --stats -d PROF_DIR/kt_<workload> -o kt -- \\
-      python3 bench.py --workload <workload> --steps 10 --warmup 3 --no-cpu --no-bf16
+      python3 bench.py --workload <workload> --no-cpu --no-bf16      (other workloads)
   rocprofv3 --kernel-trace --stats -d PROF_DIR/kt_copy -o kt -- python3 bench.py --copy-calib --steps 10
   rocprofv3 --pmc FETCH_SIZE -d PROF_DIR/pmc_FETCH_SIZE_<wl> -o pmc -- \\
       python3 bench.py --workload <workload> --steps 3 --warmup 1 --no-cpu --no-bf16
@@ -12,7 +13,7 @@ outputs of these commands (run from the repository root, TMPDIR=/tmp):
   rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE -d PROF_DIR/pmc_<C>_copy -o pmc -- \\
       python3 bench.py --copy-calib --steps 3
 
-(<wl> is the workload name with "_proj" dropped: up, down, ...). HBM bytes
+(<wl> is the workload name, with "_proj" dropped for up and down). HBM bytes
 per launch = counter KiB * 1024 * (known copy bytes / copy counter bytes).
 """
 from __future__ import annotations
@@ -24,8 +25,11 @@ import os
 import re
 import sqlite3
 
-KT_CMD = ("rocprofv3 --kernel-trace --stats -d {d}/kt_{wl} -o kt -- python3 bench.py "
-          "--workload {wl} --steps 10 --warmup 3 --no-cpu --no-bf16")
+# The default workload's trace is of the bench command itself (default steps
+# and warmup), so its average kernel durations match the bench line.
+DEFAULT_WORKLOAD = "up_proj"
+KT_CMD = "rocprofv3 --kernel-trace --stats -d {d}/kt_{wl} -o kt -- python3 bench.py"
+KT_ARGS = " --workload {wl} --no-cpu --no-bf16"
 PMC_CMD = ("rocprofv3 --pmc {c} -d {d}/pmc_{c}_{tag} -o pmc -- python3 bench.py "
            "--workload {wl} --steps 3 --warmup 1 --no-cpu --no-bf16")
 COPY_PMC_CMD = "rocprofv3 --pmc {c} -d {d}/pmc_{c}_copy -o pmc -- python3 bench.py --copy-calib --steps 3"
@@ -42,16 +46,20 @@ WORKLOAD_SHAPES = {
 
 
 def short_name(kernel: str) -> str:
+    if "gemm_i8_blockwise" in kernel:
+        return "gemm_blockwise"
     if "gemm_i8_" in kernel:
         m = re.search(r"Epilogue\)(\d)|EpilogueE(\d)", kernel)
         e = (m.group(1) or m.group(2)) if m else "?"
-        return {"0": "gemm_postscale", "1": "gemm_i32", "2": "gemm_blockwise"}.get(e, "gemm")
+        return {"0": "gemm_postscale", "1": "gemm_i32"}.get(e, "gemm")
     if "rmsnorm_quant_kernel" in kernel:
         return "rmsnorm_quant"
     if "quant_rows_long_kernel" in kernel:
         return "quant_rows_long"
     if "quant_rows_kernel" in kernel:
-        return "quant_rows_1x128" if "true" in kernel else "quant_rows"
+        # quant_rows_kernel<vectors per lane, 128-wide groups?, full rows?>
+        m = re.search(r"quant_rows_kernel<\d+, (true|false)", kernel)
+        return "quant_rows_1x128" if m and m.group(1) == "true" else "quant_rows"
     if "quant_block128" in kernel:
         return "quant_block128"
     if "copyBuffer" in kernel:
@@ -87,6 +95,8 @@ def main(prof_dir: str, out_dir: str, gemm_hash: str, quant_hash: str) -> None:
             title = "plain 1 GiB device copy (HBM calibration)"
         else:
             cmd = KT_CMD.format(d=prof_dir, wl=wl)
+            if wl != DEFAULT_WORKLOAD:
+                cmd += KT_ARGS.format(wl=wl)
             title = WORKLOAD_SHAPES.get(wl, wl)
         lines = [f"# rocprofv3 kernel trace: {wl} -- {title}", "",
                  "Command (repository root, TMPDIR=/tmp, one MI355X):", f"    {cmd}", "",
