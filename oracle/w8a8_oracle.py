@@ -33,6 +33,16 @@ R6  RMSNorm: r = 1/sqrt(mean_k x^2 + eps), eps an fp32 argument, no bias;
 R7  blockwise: 1x128 activation groups and 128x128 weight groups; for each
     128-wide K block, in ascending order, the exact block sum is scaled by
     s = fl32(sa*sw) and accumulated with an fp32 fused multiply-add.
+R11 LayerNorm prologue ("Turbodiffusion Video", "Custom Kernel Optimizations":
+    mean and variance, normalise, affine; "TurboDiffusion Integration Notes",
+    FastNorm bullet: LayerNorm and the LTX modulation helpers are fused):
+    mu = mean_k x, var = mean_k (x - mu)^2 (population variance), r =
+    1/sqrt(var + eps), both statistics from fp64 sums rounded once to fp32;
+    y = bf16(fl32(fl32(fl32(fl32(x - mu) * r) * gamma) + beta)) with an
+    optional affine; then an optional adaLN modulation in BF16 tensor
+    arithmetic, z = bf16(fl32(bf16(fl32(y * m)) + shift)), m =
+    bf16(fl32(1 + scale)), with per-channel scale and shift; then the
+    per-token quantisation of z.
 
 Floating-point values are BF16 bit patterns (uint16) at the interface.
 """
@@ -43,6 +53,7 @@ import numpy as np
 __all__ = [
     "QMAX", "BLOCK", "bf16_to_f32", "f32_to_bf16", "quantize_groups",
     "quantize_rows", "rmsnorm_inv_rms", "rmsnorm_bf16", "rmsnorm_quant",
+    "layernorm_stats", "layernorm_bf16", "modulate_bf16", "layernorm_quant",
     "gemm_i32", "postscale_bf16", "fma_f32", "gemm_blockwise_bf16",
     "w8a8_linear", "check_gemm_shape", "ShapeError", "bf16_ulp_distance",
 ]
@@ -195,6 +206,85 @@ def rmsnorm_quant(x_bits: np.ndarray, gamma_bits: np.ndarray, eps: float,
     y = rmsnorm_bf16(x_bits, gamma_bits, r)
     q, s = quantize_rows(y)
     return q, s, np.asarray(r, dtype=np.float32)
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm + adaLN modulation prologue (R11)
+# ---------------------------------------------------------------------------
+
+def layernorm_stats(x_bits: np.ndarray, eps: float):
+    """mu[m] = mean_k x[m,k] and r[m] = 1 / sqrt(mean_k (x - mu)^2 + eps).
+
+    "Turbodiffusion Video", "Custom Kernel Optimizations": a LayerNorm takes
+    the mean and the variance of each row, normalises, then applies the
+    affine step. The variance is the population one (divided by K). Both are
+    computed from fp64 sums and rounded once to fp32; eps is the fp32 value
+    the library receives. Returns (mu, r) as fp32 vectors.
+    """
+    x = bf16_to_f32(x_bits).astype(np.float64)
+    k = x.shape[1]
+    mu = np.sum(x, axis=1) / k
+    d = x - mu[:, None]
+    var = np.sum(d * d, axis=1) / k
+    eps64 = float(np.float32(eps))
+    return mu.astype(np.float32), (1.0 / np.sqrt(var + eps64)).astype(np.float32)
+
+
+def layernorm_bf16(x_bits: np.ndarray, mu: np.ndarray, r: np.ndarray,
+                   gamma_bits: np.ndarray | None = None,
+                   beta_bits: np.ndarray | None = None) -> np.ndarray:
+    """y = bf16(fl32(fl32(fl32(fl32(x - mu) * r) * gamma) + beta)).
+
+    The given per-row mu and r (fp32) are used as they are; without gamma
+    (beta) that step is left out, which is the same as gamma = 1 (beta = 0)
+    up to the sign of a zero.
+    """
+    x = bf16_to_f32(x_bits)
+    mu = np.asarray(mu, dtype=np.float32)[:, None]
+    r = np.asarray(r, dtype=np.float32)[:, None]
+    u = ((x - mu).astype(np.float32) * r).astype(np.float32)
+    if gamma_bits is not None:
+        u = (u * bf16_to_f32(gamma_bits)[None, :]).astype(np.float32)
+    if beta_bits is not None:
+        u = (u + bf16_to_f32(beta_bits)[None, :]).astype(np.float32)
+    return f32_to_bf16(u)
+
+
+def modulate_bf16(y_bits: np.ndarray, scale_bits: np.ndarray | None = None,
+                  shift_bits: np.ndarray | None = None) -> np.ndarray:
+    """adaLN modulation as BF16 tensor arithmetic, each operation rounded to BF16:
+    m = bf16(fl32(1 + scale)), z = bf16(fl32(bf16(fl32(y * m)) + shift)).
+
+    "TurboDiffusion Integration Notes", FastNorm bullet (the LTX modulation
+    helpers are fused with the norms). scale and shift are per channel; a
+    missing one leaves its step out.
+    """
+    z = bf16_to_f32(y_bits)
+    if scale_bits is not None:
+        m = bf16_to_f32(f32_to_bf16((np.float32(1) + bf16_to_f32(scale_bits)).astype(np.float32)))
+        z = bf16_to_f32(f32_to_bf16((z * m[None, :]).astype(np.float32)))
+    if shift_bits is not None:
+        z = bf16_to_f32(f32_to_bf16((z + bf16_to_f32(shift_bits)[None, :]).astype(np.float32)))
+    return f32_to_bf16(z)
+
+
+def layernorm_quant(x_bits: np.ndarray, eps: float, gamma_bits=None, beta_bits=None,
+                    scale_bits=None, shift_bits=None, mu=None, r=None):
+    """LayerNorm, adaLN modulation, then per-token quantisation.
+
+    With ``mu`` and ``r`` given (the statistics a device kernel reports),
+    everything downstream of them is recomputed from them, so codes and scales
+    can be compared bit for bit although the fp32 reduction order of the
+    statistics is not fixed. Returns (q, s, mu, r).
+    """
+    if mu is None or r is None:
+        mu0, r0 = layernorm_stats(x_bits, eps)
+        mu = mu0 if mu is None else mu
+        r = r0 if r is None else r
+    y = layernorm_bf16(x_bits, mu, r, gamma_bits, beta_bits)
+    z = modulate_bf16(y, scale_bits, shift_bits)
+    q, s = quantize_rows(z)
+    return q, s, np.asarray(mu, dtype=np.float32), np.asarray(r, dtype=np.float32)
 
 
 # ---------------------------------------------------------------------------
