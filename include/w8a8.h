@@ -92,7 +92,9 @@ w8a8_status_t w8a8_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int
  * Passage: "Reused Components", FastNorm bullet (fused RMSNorm) composed with
  * the W8A8 Linear bullet's dynamic activation quantisation.
  *
- *   r[m]  = fl32(1 / sqrt(mean_k x[m,k]^2 + eps))   (sum of squares in fp64)
+ *   r[m]  = fl32(1 / sqrt(mean_k x[m,k]^2 + eps))   (the sum of squares in fp32,
+ *           pairwise; r is within (ceil(log2 cols) + 4) * 2^-24 * r of the
+ *           correctly rounded value)
  *   y     = bf16(fl32(fl32(x * r) * gamma[k]))       (never leaves the chip)
  *   q, scale = per-token quantisation of y, as w8a8_quant_rows (1, cols).
  *
@@ -108,6 +110,45 @@ w8a8_status_t w8a8_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float
                                  int64_t rows, int64_t cols, int64_t ldx,
                                  int8_t* q, int64_t ldq, float* scale, float* inv_rms,
                                  void* stream);
+
+/*
+ * w8a8_layernorm_quant -- LayerNorm with an optional affine step and an
+ * optional adaLN modulation, fused with per-token quantisation.
+ *
+ * Passage: "Turbodiffusion Video", "Custom Kernel Optimizations" (a LayerNorm
+ * takes the row's mean and variance, normalises, then applies the affine
+ * step) and "TurboDiffusion Integration Notes", FastNorm bullet (the norms and
+ * the LTX modulation helpers are fused), composed with the W8A8 Linear
+ * bullet's dynamic activation quantisation.
+ *
+ *   mu[m]  = mean_k x[m,k],  var[m] = mean_k (x[m,k] - mu[m])^2 (divided by cols)
+ *   r[m]   = fl32(1 / sqrt(var[m] + eps))
+ *            (both sums in fp32, pairwise; mu and r are within about
+ *            (ceil(log2 cols) + 4) * 2^-24 of the correctly rounded values,
+ *            relative to mean |x| and to r)
+ *   y      = bf16(fl32(fl32(fl32(fl32(x - mu) * r) * gamma[k]) + beta[k]))
+ *   z      = bf16(fl32(bf16(fl32(y * m[k])) + shift[k])),  m = bf16(fl32(1 + scale[k]))
+ *   q, out_scale = per-token quantisation of z, as w8a8_quant_rows (1, cols).
+ *
+ *   x         [rows, cols] BF16, stride ldx  (input)
+ *   gamma     [cols] BF16 or NULL            (optional input; NULL leaves the step out)
+ *   beta      [cols] BF16 or NULL            (optional input)
+ *   mod_scale [cols] BF16 or NULL            (optional input: one sample's modulation;
+ *                                             a batch of samples is one call per sample)
+ *   mod_shift [cols] BF16 or NULL            (optional input)
+ *   q         [rows, cols] int8, stride ldq  (output)
+ *   out_scale [rows] fp32                    (output)
+ *   mean      [rows] fp32 mu, or NULL        (optional output)
+ *   rstd      [rows] fp32 r, or NULL         (optional output)
+ * Requirements as w8a8_rmsnorm_quant (every vector input 16-byte aligned).
+ * A row of zero variance with eps = 0 has r = inf and is outside the contract.
+ */
+w8a8_status_t w8a8_layernorm_quant(const uint16_t* x, const uint16_t* gamma,
+                                   const uint16_t* beta, const uint16_t* mod_scale,
+                                   const uint16_t* mod_shift, float eps,
+                                   int64_t rows, int64_t cols, int64_t ldx,
+                                   int8_t* q, int64_t ldq, float* out_scale, float* mean,
+                                   float* rstd, void* stream);
 
 /*
  * w8a8_gemm_postscale -- INT8 x INT8 GEMM, INT32 accumulation over all of K,

@@ -45,3 +45,17 @@ def check_inv_rms(r_gpu: np.ndarray, r_ref: np.ndarray, cols: int) -> float:
     assert np.all(np.isfinite(r_gpu)) and np.all(rel <= bound), \
         f"inv_rms off by {rel.max() / 2.0 ** -24:.2f} x 2^-24 (bound {bound / 2.0 ** -24:.0f})"
     return float(rel.max() / 2.0 ** -24)
+
+
+def check_ln_mean(mu_gpu: np.ndarray, mu_ref: np.ndarray, x_f32: np.ndarray) -> float:
+    """LayerNorm's mean: within (ceil(log2 K) + 4) * 2^-24 * mean|x| of the
+    oracle's (the sum's order is not fixed). Returns the largest error in
+    units of 2^-24 * mean|x|."""
+    K = x_f32.shape[1]
+    scale = np.mean(np.abs(x_f32.astype(np.float64)), axis=1)
+    bound = (int(np.ceil(np.log2(K))) + 4) * 2.0 ** -24
+    err = np.abs(np.asarray(mu_gpu, np.float64) - np.asarray(mu_ref, np.float64))
+    rel = err / np.where(scale > 0, scale, 1.0)
+    assert np.all(np.isfinite(mu_gpu)) and np.all(rel <= bound), \
+        f"mean off by {rel.max() / 2.0 ** -24:.2f} x 2^-24 mean|x|"
+    return float(rel.max() / 2.0 ** -24)

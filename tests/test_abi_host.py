@@ -34,7 +34,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert set(names) == {"w8a8_quant_rows", "w8a8_rmsnorm_quant", "w8a8_gemm_postscale",
+    assert set(names) == {"w8a8_quant_rows", "w8a8_rmsnorm_quant", "w8a8_layernorm_quant",
+                          "w8a8_gemm_postscale",
                           "w8a8_gemm_blockwise", "w8a8_gemm_i32", "w8a8_status_string",
                           "w8a8_last_error", "w8a8_version"}
     raw = ctypes.CDLL(w8.LIB_PATH)
@@ -99,6 +100,38 @@ def test_rmsnorm_quant_rejects(kwargs, status):
     assert rms(**kwargs) == status
 
 
+def ln(x=P, gamma=0x30000000, beta=0x30100000, sc=0x30200000, sh=0x30300000, eps=1e-6, rows=8,
+       cols=256, ldx=256, q=Q, ldq=256, s=S, mean=0x70000000, rstd=0x70100000):
+    return w8.lib().w8a8_layernorm_quant(x, gamma, beta, sc, sh, eps, rows, cols, ldx, q, ldq, s,
+                                         mean, rstd, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(x=None), INVALID),
+    (dict(s=None), INVALID),
+    (dict(eps=float("nan")), INVALID),
+    (dict(eps=-1.0), INVALID),
+    (dict(gamma=0x30000008), UNSUPPORTED),
+    (dict(beta=0x30100004), UNSUPPORTED),
+    (dict(sc=0x30200002), UNSUPPORTED),
+    (dict(sh=0x30300008), UNSUPPORTED),
+    (dict(mean=0x70000002), UNSUPPORTED),
+    (dict(cols=16392, ldx=16392, ldq=16400), UNSUPPORTED),          # longer than supported
+    (dict(mean=S), INVALID),                                        # mean aliases scale
+    (dict(rstd=Q + 64), INVALID),                                   # rstd inside q
+    (dict(q=0x30300000 - 256), INVALID),                            # q overlaps mod_shift
+    (dict(mean=0x70000000, rstd=0x70000000 + 16), INVALID),         # mean and rstd overlap
+])
+def test_layernorm_quant_rejects(kwargs, status):
+    assert ln(**kwargs) == status
+    assert w8.lib().w8a8_last_error() != b""
+
+
+def test_layernorm_quant_optional_vectors_may_be_null():
+    # with every optional pointer null the call only fails for its real error
+    assert ln(gamma=None, beta=None, sc=None, sh=None, mean=None, rstd=None, eps=-1.0) == INVALID
+
+
 def gemm(fn="w8a8_gemm_postscale", a=P, lda=256, w=Q, ldw=256, sa=S, sw=S + 0x100000,
          out=O, ldo=128, M=64, N=128, K=256):
     f = getattr(w8.lib(), fn)
@@ -149,6 +182,8 @@ def test_empty_calls_are_noops():
     lib = w8.lib()
     assert lib.w8a8_quant_rows(None, 0, 256, 256, 1, 256, None, 256, None, None) == OK
     assert lib.w8a8_rmsnorm_quant(None, None, 1e-6, 0, 256, 256, None, 256, None, None, None) == OK
+    assert lib.w8a8_layernorm_quant(None, None, None, None, None, 1e-6, 0, 256, 256, None, 256,
+                                    None, None, None, None) == OK
     assert lib.w8a8_gemm_postscale(None, 256, Q, 256, None, S, None, 128, 0, 128, 256, None) == OK
     assert lib.w8a8_gemm_blockwise(None, 256, Q, 256, None, S, None, 128, 0, 128, 256, None) == OK
     assert lib.w8a8_gemm_i32(None, 256, None, 256, None, 128, 0, 128, 256, None) == OK

@@ -16,7 +16,8 @@ import torch
 import oracle as O
 import workloads as W
 import w8a8_int8_quantized_token_amd as w8
-from tests.gpu_util import bf16_from_dev, bf16_to_dev, check_inv_rms, from_dev, log, to_dev
+from tests.gpu_util import (bf16_from_dev, bf16_to_dev, check_inv_rms, check_ln_mean, from_dev,
+                            log, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -189,6 +190,64 @@ def test_rmsnorm_quant_no_inv_rms_and_stride():
     sync()
     assert r is None
     assert torch.equal(q, q2) and torch.equal(s, s2)
+
+
+def layernorm_rows(shape, seed):
+    x = W.random_bits(shape, seed)
+    rows, K = shape
+    if rows >= 8:
+        x[0] = 0                                                     # zero row
+        x[1] = 0x4040                                                # constant 3.0
+        x[2] = W.random_bits((K,), seed + 1, std=1.0, mean=50.0)     # mean dominates
+        x[3] = W.random_bits((K,), seed + 2, std=1e-3)               # eps matters
+        x[4] = W.random_bits((K,), seed + 3, std=1e25)               # squares overflow fp32
+        x[5] = W.random_bits((K,), seed + 4, std=1e-22)              # squares below normals
+    return x
+
+
+@pytest.mark.parametrize("shape,seed", [((64, 256), 81), ((2048, 4096), 82), ((100, 13824), 83),
+                                        ((5, 16384), 84), ((3, 8), 85), ((777, 2048), 86),
+                                        ((40, 1000), 87)])
+def test_layernorm_quant(shape, seed):
+    log(f"layernorm_quant {shape}")
+    x = layernorm_rows(shape, seed)
+    K = shape[1]
+    g = W.random_bits((K,), seed + 10, std=0.1, mean=1.0)
+    b = W.random_bits((K,), seed + 11, std=0.1)
+    sc = W.random_bits((K,), seed + 12, std=0.2)
+    sh = W.random_bits((K,), seed + 13, std=0.2)
+    xf = O.bf16_to_f32(x)
+    for opts in (dict(), dict(g=g, b=b), dict(g=g, b=b, sc=sc, sh=sh), dict(sc=sc, sh=sh)):
+        for eps in (1e-6, 1e-5):
+            dev = {k: bf16_to_dev(v) for k, v in opts.items()}
+            q, s, mu, r = w8.w8a8_layernorm_quant(bf16_to_dev(x), eps, dev.get("g"), dev.get("b"),
+                                                  dev.get("sc"), dev.get("sh"))
+            sync()
+            mg, rg = from_dev(mu), from_dev(r)
+            mu_ref, r_ref = O.layernorm_stats(x, eps)
+            em = check_ln_mean(mg, mu_ref, xf)
+            er = check_inv_rms(rg, r_ref, K)
+            qo, so, _, _ = O.layernorm_quant(x, eps, opts.get("g"), opts.get("b"), opts.get("sc"),
+                                             opts.get("sh"), mu=mg, r=rg)
+            assert np.array_equal(from_dev(q), qo), f"codes {sorted(opts)} eps {eps}"
+            assert np.array_equal(from_dev(s).view(np.uint32), so.view(np.uint32))
+        log(f"  {sorted(opts)}: mean error {em:.2f}, r error {er:.2f} (x 2^-24)")
+
+
+def test_layernorm_quant_strided_no_stats():
+    log("layernorm_quant strided, no stats")
+    x = W.random_bits((64, 4096), 91)
+    sc = W.random_bits((4096,), 92, std=0.2)
+    xd_full = torch.zeros((64, 4096 + 64), dtype=torch.bfloat16, device="cuda")
+    xd_full[:, :4096] = bf16_to_dev(x)
+    q_full = torch.full((64, 4096 + 128), 77, dtype=torch.int8, device="cuda")
+    q, s, mu, r = w8.w8a8_layernorm_quant(xd_full[:, :4096], 1e-6, mod_scale=bf16_to_dev(sc),
+                                          q=q_full[:, :4096], stats=False)
+    q2, s2, _, _ = w8.w8a8_layernorm_quant(bf16_to_dev(x), 1e-6, mod_scale=bf16_to_dev(sc))
+    sync()
+    assert mu is None and r is None
+    assert torch.equal(q, q2) and torch.equal(s, s2)
+    assert torch.all(q_full[:, 4096:] == 77)
 
 
 GEMM_SHAPES = [((64, 128, 256), 51), ((1, 128, 128), 52), ((1000, 384, 512), 53),

@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "W8A8Error", "W8A8Unsupported", "lib", "LIB_PATH", "EXPORTED_SYMBOLS",
-    "w8a8_quant_rows", "w8a8_rmsnorm_quant", "w8a8_gemm_postscale",
+    "w8a8_quant_rows", "w8a8_rmsnorm_quant", "w8a8_layernorm_quant", "w8a8_gemm_postscale",
     "w8a8_gemm_blockwise", "w8a8_gemm_i32", "w8a8_version",
 ]
 
@@ -53,6 +53,8 @@ _st = ctypes.c_int
 _SIGS = {
     "w8a8_quant_rows": [_p, _i64, _i64, _i64, _i64, _i64, _p, _i64, _p, _p],
     "w8a8_rmsnorm_quant": [_p, _p, ctypes.c_float, _i64, _i64, _i64, _p, _i64, _p, _p, _p],
+    "w8a8_layernorm_quant": [_p, _p, _p, _p, _p, ctypes.c_float, _i64, _i64, _i64, _p, _i64, _p,
+                             _p, _p, _p],
     "w8a8_gemm_postscale": [_p, _i64, _p, _i64, _p, _p, _p, _i64, _i64, _i64, _i64, _p],
     "w8a8_gemm_blockwise": [_p, _i64, _p, _i64, _p, _p, _p, _i64, _i64, _i64, _i64, _p],
     "w8a8_gemm_i32": [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p],
@@ -166,6 +168,33 @@ def w8a8_rmsnorm_quant(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
                                  _ld(q), _ptr(scale), _ptr(inv_rms), _stream(stream))
     _check(st, "w8a8_rmsnorm_quant")
     return q, scale, inv_rms
+
+
+def w8a8_layernorm_quant(x: torch.Tensor, eps: float = 1e-6, gamma: torch.Tensor | None = None,
+                         beta: torch.Tensor | None = None, mod_scale: torch.Tensor | None = None,
+                         mod_shift: torch.Tensor | None = None, q: torch.Tensor | None = None,
+                         scale: torch.Tensor | None = None, stats: bool = True, stream=None):
+    """LayerNorm (optional gamma/beta) and adaLN modulation z = y*(1+mod_scale)+mod_shift
+    (each optional), fused with per-token INT8 quantisation.
+    Returns (q, scale, mean, rstd) (mean and rstd are None when stats is False)."""
+    _mat(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    for t, name in ((gamma, "gamma"), (beta, "beta"), (mod_scale, "mod_scale"),
+                    (mod_shift, "mod_shift")):
+        if t is not None:
+            _vec(t, torch.bfloat16, cols, name)
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    if scale is None:
+        scale = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    mean = torch.empty((rows,), dtype=torch.float32, device=x.device) if stats else None
+    rstd = torch.empty((rows,), dtype=torch.float32, device=x.device) if stats else None
+    _mat(q, torch.int8, "q")
+    st = _lib.w8a8_layernorm_quant(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(mod_scale),
+                                   _ptr(mod_shift), float(eps), rows, cols, _ld(x), _ptr(q),
+                                   _ld(q), _ptr(scale), _ptr(mean), _ptr(rstd), _stream(stream))
+    _check(st, "w8a8_layernorm_quant")
+    return q, scale, mean, rstd
 
 
 def _gemm_args(a, w, out, out_dtype):

@@ -161,6 +161,44 @@ w8a8_status_t w8a8_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float
                   "w8a8_rmsnorm_quant launch");
 }
 
+w8a8_status_t w8a8_layernorm_quant(const uint16_t* x, const uint16_t* gamma,
+                                   const uint16_t* beta, const uint16_t* mod_scale,
+                                   const uint16_t* mod_shift, float eps, int64_t rows,
+                                   int64_t cols, int64_t ldx, int8_t* q, int64_t ldq,
+                                   float* out_scale, float* mean, float* rstd, void* stream) {
+  w8a8_status_t st = check_quant_common(x, rows, cols, ldx, q, ldq, out_scale);
+  if (st != W8A8_OK) return st;
+  if (!std::isfinite(eps) || eps < 0.0f) return fail(W8A8_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if (cols > w8a8::kRmsnormMaxCols)
+    return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "cols > %lld", (long long)w8a8::kRmsnormMaxCols);
+  if (rows == 0) return ok();
+  const uint16_t* vecs[4] = {gamma, beta, mod_scale, mod_shift};
+  for (const uint16_t* v : vecs)
+    if (v && !aligned(v, 16))
+      return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "gamma, beta, mod_scale and mod_shift must be 16-byte aligned");
+  if ((mean && !aligned(mean, 4)) || (rstd && !aligned(rstd, 4)))
+    return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "mean and rstd must be 4-byte aligned");
+  const size_t xb = span_bytes(rows, cols, ldx, 2), qb = span_bytes(rows, cols, ldq, 1);
+  const size_t rb = (size_t)rows * 4, vb = (size_t)cols * 2;
+  // outputs must not overlap each other or any input
+  const void* outs[4] = {q, out_scale, mean, rstd};
+  const size_t out_bytes[4] = {qb, rb, rb, rb};
+  const void* ins[5] = {x, gamma, beta, mod_scale, mod_shift};
+  const size_t in_bytes[5] = {xb, vb, vb, vb, vb};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 5; ++j)
+      if (overlap(outs[i], out_bytes[i], ins[j], in_bytes[j]))
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "outputs overlap each other or an input");
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], out_bytes[i], outs[j], out_bytes[j]))
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "outputs overlap each other or an input");
+  }
+  return from_hip(w8a8::launch_layernorm_quant(x, gamma, beta, mod_scale, mod_shift, eps, rows,
+                                               cols, ldx, q, ldq, out_scale, mean, rstd,
+                                               (hipStream_t)stream),
+                  "w8a8_layernorm_quant launch");
+}
+
 w8a8_status_t w8a8_gemm_postscale(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
                                   const float* a_scale, const float* w_scale, uint16_t* out,
                                   int64_t ldo, int64_t M, int64_t N, int64_t K, void* stream) {

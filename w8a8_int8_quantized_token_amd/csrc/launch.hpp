@@ -18,6 +18,11 @@ hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float 
                                 int64_t cols, int64_t ldx, int8_t* q, int64_t ldq, float* scale,
                                 float* inv_rms, hipStream_t st);
 
+hipError_t launch_layernorm_quant(const uint16_t* x, const uint16_t* gamma, const uint16_t* beta,
+                                  const uint16_t* mod_scale, const uint16_t* mod_shift, float eps,
+                                  int64_t rows, int64_t cols, int64_t ldx, int8_t* q, int64_t ldq,
+                                  float* scale, float* mean, float* rstd, hipStream_t st);
+
 enum class Epilogue { kPostscaleBf16, kInt32, kBlockwiseBf16 };
 
 // Compute units of the current device (cached per device); persistent grids

@@ -375,6 +375,185 @@ void rmsnorm_quant_kernel(const uint16_t* __restrict__ x, const uint16_t* __rest
       inv_rms ? inv_rms + row : nullptr);
 }
 
+// ---------------------------------------------------------------------------
+// LayerNorm + adaLN modulation + per-token quantisation, row in registers.
+//   mu = mean(x), r = fl32(1 / sqrt(mean((x - mu)^2) + eps)), the two sums in
+//   fp32 pairwise (fp64 for rows outside the safe range);
+//   y = bf16(fl32(fl32(fl32(fl32(x - mu) * r) * gamma) + beta));
+//   z = bf16(fl32(bf16(fl32(y * m)) + shift)), m = bf16(fl32(1 + scale));
+//   codes and scale from z. gamma, beta, scale and shift are optional
+//   (a null pointer leaves the step out).
+// ---------------------------------------------------------------------------
+constexpr uint32_t kBf16OnePair = 0x3F803F80u;   // BF16 (1.0, 1.0)
+
+// Sum of the eight elements: each v_dot2 adds a BF16 pair (times 1), then a
+// pairwise tree.
+__device__ __forceinline__ float sum8_f32(const U4& v) {
+  const auto bf = [](uint32_t d) { return __builtin_bit_cast(v2bf, d); };
+  const v2bf one = bf(kBf16OnePair);
+  const float a = __builtin_amdgcn_fdot2_f32_bf16(bf(v.x), one, 0.0f, false);
+  const float b = __builtin_amdgcn_fdot2_f32_bf16(bf(v.y), one, 0.0f, false);
+  const float c = __builtin_amdgcn_fdot2_f32_bf16(bf(v.z), one, 0.0f, false);
+  const float d = __builtin_amdgcn_fdot2_f32_bf16(bf(v.w), one, 0.0f, false);
+  return (a + b) + (c + d);
+}
+
+// Sum of the eight squared deviations from mu, pairwise.
+__device__ __forceinline__ float sqdev8_f32(const U4& v, float mu) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = bf16_lo(w[i]) - mu, hi = bf16_hi(w[i]) - mu;
+    p[i] = lo * lo + hi * hi;
+  }
+  return (p[0] + p[1]) + (p[2] + p[3]);
+}
+
+// fp64 sums (of the elements, then of the squared deviations from m) for
+// rows whose fp32 sums leave the safe range. The words pass through an empty
+// asm so their unpacking is not shared with (and hoisted above this branch
+// for) the normalisation.
+__device__ __forceinline__ double sum_u4_f64(const U4& v, double s) {
+  uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  asm volatile("" : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3]));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s += (double)bf16_lo(d[i]) + (double)bf16_hi(d[i]);
+  return s;
+}
+__device__ __forceinline__ double sqdev_u4_f64(const U4& v, double m, double ss) {
+  uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  asm volatile("" : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3]));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const double a = (double)bf16_lo(d[i]) - m, b = (double)bf16_hi(d[i]) - m;
+    ss = __builtin_fma(a, a, ss);
+    ss = __builtin_fma(b, b, ss);
+  }
+  return ss;
+}
+
+// y and the modulation for eight elements (pairs stay packed as BF16).
+__device__ __forceinline__ U4 layernorm_u4(const U4& v, float mu, float r, const U4* g,
+                                           const U4* b, const U4* sc, const U4* sh) {
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  const uint32_t gw[4] = {g ? g->x : 0u, g ? g->y : 0u, g ? g->z : 0u, g ? g->w : 0u};
+  const uint32_t bw[4] = {b ? b->x : 0u, b ? b->y : 0u, b ? b->z : 0u, b ? b->w : 0u};
+  const uint32_t cw[4] = {sc ? sc->x : 0u, sc ? sc->y : 0u, sc ? sc->z : 0u, sc ? sc->w : 0u};
+  const uint32_t hw[4] = {sh ? sh->x : 0u, sh ? sh->y : 0u, sh ? sh->z : 0u, sh ? sh->w : 0u};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float lo = (bf16_lo(d[i]) - mu) * r;
+    float hi = (bf16_hi(d[i]) - mu) * r;
+    if (g) {
+      lo = lo * bf16_lo(gw[i]);
+      hi = hi * bf16_hi(gw[i]);
+    }
+    if (b) {
+      lo = lo + bf16_lo(bw[i]);
+      hi = hi + bf16_hi(bw[i]);
+    }
+    uint32_t y = pack_bf16x2(lo, hi);
+    if (sc) {
+      const uint32_t m = pack_bf16x2(1.0f + bf16_lo(cw[i]), 1.0f + bf16_hi(cw[i]));
+      y = pack_bf16x2(bf16_lo(y) * bf16_lo(m), bf16_hi(y) * bf16_hi(m));
+    }
+    if (sh) y = pack_bf16x2(bf16_lo(y) + bf16_lo(hw[i]), bf16_hi(y) + bf16_hi(hw[i]));
+    o[i] = y;
+  }
+  return U4{o[0], o[1], o[2], o[3]};
+}
+
+template <int kVpl, bool kFull>
+__global__ __launch_bounds__(kRowsPerBlock * kWave)
+void layernorm_quant_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
+                            const uint16_t* __restrict__ beta,
+                            const uint16_t* __restrict__ mod_scale,
+                            const uint16_t* __restrict__ mod_shift, float eps, int64_t rows,
+                            int64_t cols, int64_t ldx, int8_t* __restrict__ q, int64_t ldq,
+                            float* __restrict__ scale, float* __restrict__ mean_out,
+                            float* __restrict__ rstd_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int nvec = (int)(cols >> 3);
+  U4 v[kVpl];
+  load_row<kVpl, kFull>(v, reinterpret_cast<const U4*>(x + row * ldx), lane, nvec);
+  // Statistics: the mean from pairwise fp32 sums of the elements, then the
+  // sum of squared deviations about that fp32 mean (padding vectors left
+  // out). Both terms are non-negative or cancel only through the mean, so
+  // each is within about (log2(cols) + 6) * 2^-24 of the exact value,
+  // relative to the sum of |x| and the sum of squares respectively.
+  float part[kVpl];
+#pragma unroll
+  for (int j = 0; j < kVpl; ++j) part[j] = sum8_f32(v[j]);
+  const float s1 = wave_sum_f32(tree_sum<0, kVpl>(part));
+  float mu = (float)((double)s1 / (double)cols);
+#pragma unroll
+  for (int j = 0; j < kVpl; ++j)
+    part[j] = has_vec<kVpl, kFull>(lane, j, nvec) ? sqdev8_f32(v[j], mu) : 0.0f;
+  const float s2 = wave_sum_f32(tree_sum<0, kVpl>(part));
+  double var;
+  if (__builtin_isfinite(s1) && s2 >= 0x1p-80f && s2 <= 0x1p100f) {
+    var = (double)s2 / (double)cols;
+  } else {
+    double s = 0.0, ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < kVpl; ++j) s = sum_u4_f64(v[j], s);   // padding vectors are zero
+    const double m64 = wave_sum_f64(s) / (double)cols;
+#pragma unroll
+    for (int j = 0; j < kVpl; ++j)
+      if (has_vec<kVpl, kFull>(lane, j, nvec)) ss = sqdev_u4_f64(v[j], m64, ss);
+    var = wave_sum_f64(ss) / (double)cols;
+    mu = (float)m64;
+  }
+  const float r = (float)(1.0 / __builtin_sqrt(var + (double)eps));
+  // normalise, modulate (optional vectors read per 16-byte vector from L2)
+  const U4* gr = reinterpret_cast<const U4*>(gamma);
+  const U4* br = reinterpret_cast<const U4*>(beta);
+  const U4* cr = reinterpret_cast<const U4*>(mod_scale);
+  const U4* hr = reinterpret_cast<const U4*>(mod_shift);
+  uint32_t m2 = 0;
+#pragma unroll
+  for (int j = 0; j < kVpl; ++j) {
+    const int idx0 = lane + j * kWave;
+    const int idx = kFull || idx0 < nvec ? idx0 : nvec - 1;
+    U4 gv, bv, cv, hv;
+    if (gr) gv = gr[idx];
+    if (br) bv = br[idx];
+    if (cr) cv = cr[idx];
+    if (hr) hv = hr[idx];
+    const U4 z = layernorm_u4(v[j], mu, r, gr ? &gv : nullptr, br ? &bv : nullptr,
+                              cr ? &cv : nullptr, hr ? &hv : nullptr);
+    v[j] = has_vec<kVpl, kFull>(lane, j, nvec) ? z : U4{0u, 0u, 0u, 0u};
+    m2 = absmax2_u4(v[j], m2);
+  }
+  const uint32_t m = wave_max_u32(fold_absmax(m2));
+  const QuantParams p = quant_params(bf16_bits_to_float(m));
+  uint2* qr = reinterpret_cast<uint2*>(q + row * ldq);
+  if (p.fast) store_row_codes<kVpl, kFull, true>(v, qr, lane, nvec, p);
+  else store_row_codes<kVpl, kFull, false>(v, qr, lane, nvec, p);
+  if (lane == 0) {
+    scale[row] = p.s;
+    if (mean_out) mean_out[row] = mu;
+    if (rstd_out) rstd_out[row] = r;
+  }
+}
+
+template <int kVpl, bool kFull>
+static hipError_t launch_layernorm(const uint16_t* x, const uint16_t* gamma, const uint16_t* beta,
+                                   const uint16_t* mod_scale, const uint16_t* mod_shift,
+                                   float eps, int64_t rows, int64_t cols, int64_t ldx, int8_t* q,
+                                   int64_t ldq, float* scale, float* mean, float* rstd,
+                                   hipStream_t st) {
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  hipLaunchKernelGGL((layernorm_quant_kernel<kVpl, kFull>), grid, dim3(kRowsPerBlock * kWave), 0,
+                     st, x, gamma, beta, mod_scale, mod_shift, eps, rows, cols, ldx, q, ldq,
+                     scale, mean, rstd);
+  return hipGetLastError();
+}
+
 template <int kVpl, bool kFull>
 static hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int64_t rows,
                                  int64_t cols, int64_t ldx, int8_t* q, int64_t ldq, float* scale,
@@ -460,6 +639,21 @@ hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float 
   launch_rmsnorm<V, F>(x, gamma, eps, rows, cols, ldx, q, ldq, scale, inv_rms, st)
   W8A8_VPL_SWITCH(vpl, W8A8_CALL_RMS)
 #undef W8A8_CALL_RMS
+  return hipErrorInvalidValue;   // host validation rejects longer rows first
+}
+
+hipError_t launch_layernorm_quant(const uint16_t* x, const uint16_t* gamma, const uint16_t* beta,
+                                  const uint16_t* mod_scale, const uint16_t* mod_shift, float eps,
+                                  int64_t rows, int64_t cols, int64_t ldx, int8_t* q, int64_t ldq,
+                                  float* scale, float* mean, float* rstd, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const int vpl = pick_vpl(cols >> 3);
+  const bool full = vpl > 0 && (cols >> 3) == (int64_t)vpl * kWave;
+#define W8A8_CALL_LN(V, F)                                                                  \
+  launch_layernorm<V, F>(x, gamma, beta, mod_scale, mod_shift, eps, rows, cols, ldx, q, ldq, \
+                         scale, mean, rstd, st)
+  W8A8_VPL_SWITCH(vpl, W8A8_CALL_LN)
+#undef W8A8_CALL_LN
   return hipErrorInvalidValue;   // host validation rejects longer rows first
 }
 
