@@ -134,6 +134,8 @@ def main():
     x_host = W.x_bits(wl)
     w_host = W.w_bits(wl)
     gamma = up(W.gamma_bits(wl)) if wl.norm else None
+    mod_scale = up(W.mod_bits(wl, "mod_scale")) if wl.layernorm else None
+    mod_shift = up(W.mod_bits(wl, "mod_shift")) if wl.layernorm else None
     xs = [up(x_host)]
     for _ in range(N_ROTATE - 1):
         xs.append(xs[0].clone())
@@ -158,6 +160,7 @@ def main():
     else:
         sa = torch.empty((M,), dtype=torch.float32, device=dev)
     inv = torch.empty((M,), dtype=torch.float32, device=dev)
+    mean = torch.empty((M,), dtype=torch.float32, device=dev)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
     if wl.norm:
@@ -165,6 +168,13 @@ def main():
         def quant(x):
             w8.w8a8_rmsnorm_quant(x, gamma, wl.eps, q=qa, scale=sa, inv_rms=inv)
         quant_bytes = 3 * M * K + 4 * M + 2 * K + 4 * M     # read x, gamma; write q, scale, inv_rms
+    elif wl.layernorm:
+        quant_name = "layernorm_quant"
+        def quant(x):
+            w8.w8a8_layernorm_quant(x, wl.eps, mod_scale=mod_scale, mod_shift=mod_shift, q=qa,
+                                    scale=sa, mean=mean, rstd=inv)
+        # read x, the two modulation vectors; write q, scale, mean, rstd
+        quant_bytes = 3 * M * K + 4 * K + 4 * M + 8 * M
     elif wl.blockwise:
         quant_name = "quant_rows_1x128"
         def quant(x):
@@ -290,15 +300,20 @@ def cpu_baseline(wl, x_host, w_host, budget_s):
     chunk = 256
     t_path = 0.0
     g = None
-    if wl.norm:
+    if wl.norm or wl.layernorm:
         import workloads as W
-        g = W.gamma_bits(wl)
+        g = W.gamma_bits(wl) if wl.norm else None
+        msc = W.mod_bits(wl, "mod_scale") if wl.layernorm else None
+        msh = W.mod_bits(wl, "mod_shift") if wl.layernorm else None
     while rows_done < wl.M and t_path < budget_s:
         r1 = min(rows_done + chunk, wl.M)
         x = x_host[rows_done:r1]
         t1 = time.perf_counter()
         if wl.norm:
             qa, sa, _ = O.rmsnorm_quant(x, g, wl.eps)
+            O.postscale_bf16(O.gemm_i32(qa, qw), sa, sw)
+        elif wl.layernorm:
+            qa, sa, _, _ = O.layernorm_quant(x, wl.eps, scale_bits=msc, shift_bits=msh)
             O.postscale_bf16(O.gemm_i32(qa, qw), sa, sw)
         elif wl.blockwise:
             qa, sa = O.quantize_groups(x, 1, 128)

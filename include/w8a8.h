@@ -140,8 +140,9 @@ w8a8_status_t w8a8_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float
  *   out_scale [rows] fp32                    (output)
  *   mean      [rows] fp32 mu, or NULL        (optional output)
  *   rstd      [rows] fp32 r, or NULL         (optional output)
- * Requirements as w8a8_rmsnorm_quant (every vector input 16-byte aligned).
- * A row of zero variance with eps = 0 has r = inf and is outside the contract.
+ * Requirements as w8a8_rmsnorm_quant (every vector input 16-byte aligned),
+ * with cols <= 8192 (else W8A8_ERR_UNSUPPORTED_SHAPE). A row of zero variance
+ * with eps = 0 has r = inf and is outside the contract.
  */
 w8a8_status_t w8a8_layernorm_quant(const uint16_t* x, const uint16_t* gamma,
                                    const uint16_t* beta, const uint16_t* mod_scale,

@@ -41,6 +41,7 @@ WORKLOAD_SHAPES = {
     "square": "M=N=K=4096 (quant -> post-scale GEMM)",
     "blockwise_small": "M=1000 N=K=5120 (1x128 quant -> blockwise GEMM)",
     "blockwise_large": "M=32760 N=K=5120 (1x128 quant -> blockwise GEMM)",
+    "ln_up_proj": "M=28672 N=16384 K=4096 (LayerNorm+modulation+quant -> post-scale GEMM)",
     "tiny": "M=64 N=128 K=256",
 }
 
@@ -54,6 +55,8 @@ def short_name(kernel: str) -> str:
         return {"0": "gemm_postscale", "1": "gemm_i32"}.get(e, "gemm")
     if "rmsnorm_quant_kernel" in kernel:
         return "rmsnorm_quant"
+    if "layernorm_quant_kernel" in kernel:
+        return "layernorm_quant"
     if "quant_rows_long_kernel" in kernel:
         return "quant_rows_long"
     if "quant_rows_kernel" in kernel:
@@ -139,7 +142,7 @@ def main(prof_dir: str, out_dir: str, gemm_hash: str, quant_hash: str) -> None:
             wv = write.get((k, g), [])
             wb = (sum(wv) / len(wv) * 1024 * calib["WRITE_SIZE"]) if wv else float("nan")
             lines.append(f"{k:<18} {len(vs):>8} {fb / 1e6:>10.1f} {wb / 1e6:>10.1f} {(fb + wb) / 1e6:>10.1f}")
-            if k.startswith("gemm") or k.startswith("rmsnorm") or k.startswith("quant"):
+            if k.startswith(("gemm", "rmsnorm", "layernorm", "quant")):
                 src = gemm_hash if k.startswith("gemm") else quant_hash
                 with open(os.path.join(out_dir, f"traffic_{k}_{wl}.json"), "w") as f:
                     json.dump({"kernel": k, "workload": wl, "hbm_bytes_per_launch": round(fb + wb),

@@ -116,7 +116,7 @@ def ln(x=P, gamma=0x30000000, beta=0x30100000, sc=0x30200000, sh=0x30300000, eps
     (dict(sc=0x30200002), UNSUPPORTED),
     (dict(sh=0x30300008), UNSUPPORTED),
     (dict(mean=0x70000002), UNSUPPORTED),
-    (dict(cols=16392, ldx=16392, ldq=16400), UNSUPPORTED),          # longer than supported
+    (dict(cols=8200, ldx=8200, ldq=8200), UNSUPPORTED),             # longer than supported
     (dict(mean=S), INVALID),                                        # mean aliases scale
     (dict(rstd=Q + 64), INVALID),                                   # rstd inside q
     (dict(q=0x30300000 - 256), INVALID),                            # q overlaps mod_shift

@@ -19,7 +19,7 @@ import torch
 import oracle as O
 import workloads as W
 import w8a8_int8_quantized_token_amd as w8
-from tests.gpu_util import bf16_from_dev, bf16_to_dev, check_inv_rms, from_dev, log
+from tests.gpu_util import bf16_from_dev, bf16_to_dev, check_inv_rms, check_ln_mean, from_dev, log
 
 pytestmark = pytest.mark.gpu
 
@@ -41,7 +41,7 @@ def ulp_check(got, ref, what):
 
 
 @pytest.mark.parametrize("name", ["square", "up_proj", "down_proj", "blockwise_small",
-                                  "blockwise_large"])
+                                  "blockwise_large", "ln_up_proj"])
 def test_workload_full_size(name):
     wl = W.WORKLOADS[name]
     M, N, K = wl.M, wl.N, wl.K
@@ -67,6 +67,10 @@ def test_workload_full_size(name):
     if wl.norm:
         g = W.gamma_bits(wl)
         qa, sa, r = w8.w8a8_rmsnorm_quant(xd, bf16_to_dev(g), wl.eps)
+    elif wl.layernorm:
+        msc, msh = W.mod_bits(wl, "mod_scale"), W.mod_bits(wl, "mod_shift")
+        qa, sa, mu, r = w8.w8a8_layernorm_quant(xd, wl.eps, mod_scale=bf16_to_dev(msc),
+                                                mod_shift=bf16_to_dev(msh))
     elif wl.blockwise:
         qa, sa = w8.w8a8_quant_rows(xd, 1, 128)
     else:
@@ -88,6 +92,13 @@ def test_workload_full_size(name):
         rref = O.rmsnorm_inv_rms(xs, wl.eps)
         check_inv_rms(rg, rref, K)
         qa_o, sa_o, _ = O.rmsnorm_quant(xs, g, wl.eps, r=rg)
+    elif wl.layernorm:
+        mg, rg = from_dev(mu)[rows], from_dev(r)[rows]
+        mu_ref, r_ref = O.layernorm_stats(xs, wl.eps)
+        check_ln_mean(mg, mu_ref, O.bf16_to_f32(xs))
+        check_inv_rms(rg, r_ref, K)
+        qa_o, sa_o, _, _ = O.layernorm_quant(xs, wl.eps, scale_bits=msc, shift_bits=msh,
+                                             mu=mg, r=rg)
     elif wl.blockwise:
         qa_o, sa_o = O.quantize_groups(xs, 1, 128)
     else:

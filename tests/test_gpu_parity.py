@@ -205,9 +205,9 @@ def layernorm_rows(shape, seed):
     return x
 
 
-@pytest.mark.parametrize("shape,seed", [((64, 256), 81), ((2048, 4096), 82), ((100, 13824), 83),
-                                        ((5, 16384), 84), ((3, 8), 85), ((777, 2048), 86),
-                                        ((40, 1000), 87)])
+@pytest.mark.parametrize("shape,seed", [((64, 256), 81), ((2048, 4096), 82), ((100, 5120), 83),
+                                        ((5, 8192), 84), ((3, 8), 85), ((777, 2048), 86),
+                                        ((40, 1000), 87), ((9, 6144), 88)])
 def test_layernorm_quant(shape, seed):
     log(f"layernorm_quant {shape}")
     x = layernorm_rows(shape, seed)
@@ -232,6 +232,12 @@ def test_layernorm_quant(shape, seed):
             assert np.array_equal(from_dev(q), qo), f"codes {sorted(opts)} eps {eps}"
             assert np.array_equal(from_dev(s).view(np.uint32), so.view(np.uint32))
         log(f"  {sorted(opts)}: mean error {em:.2f}, r error {er:.2f} (x 2^-24)")
+
+
+def test_layernorm_quant_long_rows_unsupported():
+    x = torch.zeros((2, 8200), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(w8.W8A8Unsupported):
+        w8.w8a8_layernorm_quant(x, 1e-6)
 
 
 def test_layernorm_quant_strided_no_stats():

@@ -173,10 +173,13 @@ def w8a8_rmsnorm_quant(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
 def w8a8_layernorm_quant(x: torch.Tensor, eps: float = 1e-6, gamma: torch.Tensor | None = None,
                          beta: torch.Tensor | None = None, mod_scale: torch.Tensor | None = None,
                          mod_shift: torch.Tensor | None = None, q: torch.Tensor | None = None,
-                         scale: torch.Tensor | None = None, stats: bool = True, stream=None):
+                         scale: torch.Tensor | None = None, stats: bool = True,
+                         mean: torch.Tensor | None = None, rstd: torch.Tensor | None = None,
+                         stream=None):
     """LayerNorm (optional gamma/beta) and adaLN modulation z = y*(1+mod_scale)+mod_shift
     (each optional), fused with per-token INT8 quantisation.
-    Returns (q, scale, mean, rstd) (mean and rstd are None when stats is False)."""
+    Returns (q, scale, mean, rstd) (mean and rstd are None when stats is False;
+    given mean/rstd tensors are written in place)."""
     _mat(x, torch.bfloat16, "x")
     rows, cols = x.shape
     for t, name in ((gamma, "gamma"), (beta, "beta"), (mod_scale, "mod_scale"),
@@ -187,8 +190,13 @@ def w8a8_layernorm_quant(x: torch.Tensor, eps: float = 1e-6, gamma: torch.Tensor
         q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
     if scale is None:
         scale = torch.empty((rows,), dtype=torch.float32, device=x.device)
-    mean = torch.empty((rows,), dtype=torch.float32, device=x.device) if stats else None
-    rstd = torch.empty((rows,), dtype=torch.float32, device=x.device) if stats else None
+    if stats:
+        mean = torch.empty((rows,), dtype=torch.float32, device=x.device) if mean is None else mean
+        rstd = torch.empty((rows,), dtype=torch.float32, device=x.device) if rstd is None else rstd
+        _vec(mean, torch.float32, rows, "mean")
+        _vec(rstd, torch.float32, rows, "rstd")
+    else:
+        mean = rstd = None
     _mat(q, torch.int8, "q")
     st = _lib.w8a8_layernorm_quant(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(mod_scale),
                                    _ptr(mod_shift), float(eps), rows, cols, _ld(x), _ptr(q),

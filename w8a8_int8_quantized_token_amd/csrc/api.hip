@@ -169,8 +169,8 @@ w8a8_status_t w8a8_layernorm_quant(const uint16_t* x, const uint16_t* gamma,
   w8a8_status_t st = check_quant_common(x, rows, cols, ldx, q, ldq, out_scale);
   if (st != W8A8_OK) return st;
   if (!std::isfinite(eps) || eps < 0.0f) return fail(W8A8_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
-  if (cols > w8a8::kRmsnormMaxCols)
-    return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "cols > %lld", (long long)w8a8::kRmsnormMaxCols);
+  if (cols > w8a8::kLayernormMaxCols)
+    return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "cols > %lld", (long long)w8a8::kLayernormMaxCols);
   if (rows == 0) return ok();
   const uint16_t* vecs[4] = {gamma, beta, mod_scale, mod_shift};
   for (const uint16_t* v : vecs)

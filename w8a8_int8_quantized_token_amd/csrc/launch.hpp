@@ -9,6 +9,10 @@ namespace w8a8 {
 // Longest row the register-resident RMSNorm kernel holds (32 vectors of
 // eight BF16 per lane, 64 lanes).
 constexpr int64_t kRmsnormMaxCols = 32 * 64 * 8;
+// ... and the LayerNorm kernel (16 vectors per lane; DiT hidden sizes are
+// 4096 and 5120).
+constexpr int kLayernormMaxVpl = 16;
+constexpr int64_t kLayernormMaxCols = kLayernormMaxVpl * 64 * 8;
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                              int64_t group_rows, int64_t group_cols, int8_t* q, int64_t ldq,

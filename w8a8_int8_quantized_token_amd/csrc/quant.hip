@@ -433,40 +433,54 @@ __device__ __forceinline__ double sqdev_u4_f64(const U4& v, double m, double ss)
   return ss;
 }
 
-// y and the modulation for eight elements (pairs stay packed as BF16).
-__device__ __forceinline__ U4 layernorm_u4(const U4& v, float mu, float r, const U4* g,
-                                           const U4* b, const U4* sc, const U4* sh) {
+// y and the modulation for eight elements (pairs stay packed as BF16). The
+// affine step and the modulation are compile-time choices; a missing half of
+// either comes in as its identity (gamma 1, beta 0, m 1, shift 0), which
+// changes nothing but the sign of a zero, and no code depends on that. m is
+// the packed bf16(fl32(1 + scale)), formed once per workgroup.
+template <bool kAffine, bool kMod>
+__device__ __forceinline__ U4 layernorm_u4(const U4& v, float mu, float r, const U4& g,
+                                           const U4& b, const U4& m, const U4& sh) {
   const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-  const uint32_t gw[4] = {g ? g->x : 0u, g ? g->y : 0u, g ? g->z : 0u, g ? g->w : 0u};
-  const uint32_t bw[4] = {b ? b->x : 0u, b ? b->y : 0u, b ? b->z : 0u, b ? b->w : 0u};
-  const uint32_t cw[4] = {sc ? sc->x : 0u, sc ? sc->y : 0u, sc ? sc->z : 0u, sc ? sc->w : 0u};
-  const uint32_t hw[4] = {sh ? sh->x : 0u, sh ? sh->y : 0u, sh ? sh->z : 0u, sh ? sh->w : 0u};
+  const uint32_t gw[4] = {g.x, g.y, g.z, g.w}, bw[4] = {b.x, b.y, b.z, b.w};
+  const uint32_t mw[4] = {m.x, m.y, m.z, m.w}, hw[4] = {sh.x, sh.y, sh.z, sh.w};
   uint32_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float lo = (bf16_lo(d[i]) - mu) * r;
     float hi = (bf16_hi(d[i]) - mu) * r;
-    if (g) {
-      lo = lo * bf16_lo(gw[i]);
-      hi = hi * bf16_hi(gw[i]);
-    }
-    if (b) {
-      lo = lo + bf16_lo(bw[i]);
-      hi = hi + bf16_hi(bw[i]);
+    if constexpr (kAffine) {
+      lo = lo * bf16_lo(gw[i]) + bf16_lo(bw[i]);
+      hi = hi * bf16_hi(gw[i]) + bf16_hi(bw[i]);
     }
     uint32_t y = pack_bf16x2(lo, hi);
-    if (sc) {
-      const uint32_t m = pack_bf16x2(1.0f + bf16_lo(cw[i]), 1.0f + bf16_hi(cw[i]));
-      y = pack_bf16x2(bf16_lo(y) * bf16_lo(m), bf16_hi(y) * bf16_hi(m));
+    if constexpr (kMod) {
+      y = pack_bf16x2(bf16_lo(y) * bf16_lo(mw[i]), bf16_hi(y) * bf16_hi(mw[i]));
+      y = pack_bf16x2(bf16_lo(y) + bf16_lo(hw[i]), bf16_hi(y) + bf16_hi(hw[i]));
     }
-    if (sh) y = pack_bf16x2(bf16_lo(y) + bf16_lo(hw[i]), bf16_hi(y) + bf16_hi(hw[i]));
     o[i] = y;
   }
   return U4{o[0], o[1], o[2], o[3]};
 }
 
-template <int kVpl, bool kFull>
-__global__ __launch_bounds__(kRowsPerBlock * kWave)
+// packed bf16(fl32(1 + scale)) of a vector of scale pairs
+__device__ __forceinline__ U4 one_plus_bf16(const U4& c) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(1.0f + bf16_lo(w[i]), 1.0f + bf16_hi(w[i]));
+  return U4{o[0], o[1], o[2], o[3]};
+}
+
+constexpr int kLnRowsPerBlock = 8;   // rows (waves) sharing the staged vectors
+
+// 16-byte vector idx of an optional [cols] BF16 vector, or its identity value.
+__device__ __forceinline__ U4 opt_vec(const U4* p, int idx, uint32_t identity) {
+  return p ? p[idx] : U4{identity, identity, identity, identity};
+}
+
+template <int kVpl, bool kFull, bool kAffine, bool kMod>
+__global__ __launch_bounds__(kLnRowsPerBlock * kWave)
 void layernorm_quant_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
                             const uint16_t* __restrict__ beta,
                             const uint16_t* __restrict__ mod_scale,
@@ -474,17 +488,41 @@ void layernorm_quant_kernel(const uint16_t* __restrict__ x, const uint16_t* __re
                             int64_t cols, int64_t ldx, int8_t* __restrict__ q, int64_t ldq,
                             float* __restrict__ scale, float* __restrict__ mean_out,
                             float* __restrict__ rstd_out) {
+  // The per-channel vectors of the affine step and the modulation, staged
+  // once per workgroup in LDS (with m = bf16(1 + scale) formed here), so each
+  // row reads them from LDS instead of L2.
+  constexpr int kStaged = (kAffine ? 2 : 0) + (kMod ? 2 : 0);
+  __shared__ __attribute__((aligned(16))) U4 staged[kStaged > 0 ? kStaged : 1][kVpl * kWave];
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  const int64_t row = (int64_t)blockIdx.x * kLnRowsPerBlock + (threadIdx.x >> 6);
   const int nvec = (int)(cols >> 3);
   U4 v[kVpl];
-  load_row<kVpl, kFull>(v, reinterpret_cast<const U4*>(x + row * ldx), lane, nvec);
+  if (row < rows)   // the row's loads go out first; the whole workgroup stages below
+    load_row<kVpl, kFull>(v, reinterpret_cast<const U4*>(x + row * ldx), lane, nvec);
+  if constexpr (kStaged > 0) {
+    const U4* gr = reinterpret_cast<const U4*>(gamma);
+    const U4* br = reinterpret_cast<const U4*>(beta);
+    const U4* cr = reinterpret_cast<const U4*>(mod_scale);
+    const U4* hr = reinterpret_cast<const U4*>(mod_shift);
+    for (int i = threadIdx.x; i < kVpl * kWave; i += kLnRowsPerBlock * kWave) {
+      const int idx = i < nvec ? i : nvec - 1;
+      int t = 0;
+      if constexpr (kAffine) {
+        staged[t++][i] = opt_vec(gr, idx, kBf16OnePair);
+        staged[t++][i] = opt_vec(br, idx, 0u);
+      }
+      if constexpr (kMod) {
+        staged[t++][i] = one_plus_bf16(opt_vec(cr, idx, 0u));
+        staged[t++][i] = opt_vec(hr, idx, 0u);
+      }
+    }
+    __syncthreads();
+  }
+  if (row >= rows) return;
   // Statistics: the mean from pairwise fp32 sums of the elements, then the
   // sum of squared deviations about that fp32 mean (padding vectors left
-  // out). Both terms are non-negative or cancel only through the mean, so
-  // each is within about (log2(cols) + 6) * 2^-24 of the exact value,
-  // relative to the sum of |x| and the sum of squares respectively.
+  // out). Each is within about (log2(cols) + 6) * 2^-24 of the exact value,
+  // relative to the sum of |x| and to the sum of squares respectively.
   float part[kVpl];
 #pragma unroll
   for (int j = 0; j < kVpl; ++j) part[j] = sum8_f32(v[j]);
@@ -509,25 +547,29 @@ void layernorm_quant_kernel(const uint16_t* __restrict__ x, const uint16_t* __re
     mu = (float)m64;
   }
   const float r = (float)(1.0 / __builtin_sqrt(var + (double)eps));
-  // normalise, modulate (optional vectors read per 16-byte vector from L2)
-  const U4* gr = reinterpret_cast<const U4*>(gamma);
-  const U4* br = reinterpret_cast<const U4*>(beta);
-  const U4* cr = reinterpret_cast<const U4*>(mod_scale);
-  const U4* hr = reinterpret_cast<const U4*>(mod_shift);
+  // The row passes through an empty asm: otherwise the compiler keeps the
+  // variance pass's x - mu values for the normalisation, all of the row's
+  // differences live at once instead of its packed words.
+#pragma unroll
+  for (int j = 0; j < kVpl; ++j)
+    asm volatile("" : "+v"(v[j].x), "+v"(v[j].y), "+v"(v[j].z), "+v"(v[j].w));
+  // normalise, modulate
   uint32_t m2 = 0;
 #pragma unroll
   for (int j = 0; j < kVpl; ++j) {
-    const int idx0 = lane + j * kWave;
-    const int idx = kFull || idx0 < nvec ? idx0 : nvec - 1;
-    U4 gv, bv, cv, hv;
-    if (gr) gv = gr[idx];
-    if (br) bv = br[idx];
-    if (cr) cv = cr[idx];
-    if (hr) hv = hr[idx];
-    const U4 z = layernorm_u4(v[j], mu, r, gr ? &gv : nullptr, br ? &bv : nullptr,
-                              cr ? &cv : nullptr, hr ? &hv : nullptr);
-    v[j] = has_vec<kVpl, kFull>(lane, j, nvec) ? z : U4{0u, 0u, 0u, 0u};
+    const int i = lane + j * kWave;
+    const U4 zero{0u, 0u, 0u, 0u};
+    const U4 gv = kAffine ? staged[0][i] : zero;
+    const U4 bv = kAffine ? staged[1][i] : zero;
+    const U4 mv = kMod ? staged[kAffine ? 2 : 0][i] : zero;
+    const U4 hv = kMod ? staged[kAffine ? 3 : 1][i] : zero;
+    const U4 z = layernorm_u4<kAffine, kMod>(v[j], mu, r, gv, bv, mv, hv);
+    v[j] = has_vec<kVpl, kFull>(lane, j, nvec) ? z : zero;
     m2 = absmax2_u4(v[j], m2);
+    // keep the staged-vector reads to four vectors ahead: the scheduler would
+    // otherwise hoist them all and hold them with the whole row
+    if constexpr (kVpl >= 8)
+      if (j % 4 == 3) __builtin_amdgcn_sched_barrier(0);
   }
   const uint32_t m = wave_max_u32(fold_absmax(m2));
   const QuantParams p = quant_params(bf16_bits_to_float(m));
@@ -547,10 +589,17 @@ static hipError_t launch_layernorm(const uint16_t* x, const uint16_t* gamma, con
                                    float eps, int64_t rows, int64_t cols, int64_t ldx, int8_t* q,
                                    int64_t ldq, float* scale, float* mean, float* rstd,
                                    hipStream_t st) {
-  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-  hipLaunchKernelGGL((layernorm_quant_kernel<kVpl, kFull>), grid, dim3(kRowsPerBlock * kWave), 0,
-                     st, x, gamma, beta, mod_scale, mod_shift, eps, rows, cols, ldx, q, ldq,
-                     scale, mean, rstd);
+  const dim3 grid((unsigned)((rows + kLnRowsPerBlock - 1) / kLnRowsPerBlock));
+  const dim3 block(kLnRowsPerBlock * kWave);
+  const bool affine = gamma || beta, mod = mod_scale || mod_shift;
+#define W8A8_LN_LAUNCH(A, M)                                                                   \
+  hipLaunchKernelGGL((layernorm_quant_kernel<kVpl, kFull, A, M>), grid, block, 0, st, x, gamma, \
+                     beta, mod_scale, mod_shift, eps, rows, cols, ldx, q, ldq, scale, mean, rstd)
+  if (affine && mod) W8A8_LN_LAUNCH(true, true);
+  else if (affine) W8A8_LN_LAUNCH(true, false);
+  else if (mod) W8A8_LN_LAUNCH(false, true);
+  else W8A8_LN_LAUNCH(false, false);
+#undef W8A8_LN_LAUNCH
   return hipGetLastError();
 }
 
@@ -647,12 +696,21 @@ hipError_t launch_layernorm_quant(const uint16_t* x, const uint16_t* gamma, cons
                                   int64_t rows, int64_t cols, int64_t ldx, int8_t* q, int64_t ldq,
                                   float* scale, float* mean, float* rstd, hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  const int vpl = pick_vpl(cols >> 3);
-  const bool full = vpl > 0 && (cols >> 3) == (int64_t)vpl * kWave;
+  // vectors per lane: the smallest power of two that holds the row (fewer
+  // instantiations than the quant kernels' list; other rows run masked)
+  const int64_t nvec = cols >> 3;
+  int vpl = 1;
+  while ((int64_t)vpl * kWave < nvec && vpl < kLayernormMaxVpl) vpl *= 2;
+  const bool full = nvec == (int64_t)vpl * kWave;
 #define W8A8_CALL_LN(V, F)                                                                  \
   launch_layernorm<V, F>(x, gamma, beta, mod_scale, mod_shift, eps, rows, cols, ldx, q, ldq, \
                          scale, mean, rstd, st)
-  W8A8_VPL_SWITCH(vpl, W8A8_CALL_LN)
+  switch (vpl) {
+    W8A8_VPL_CASE(1, W8A8_CALL_LN) W8A8_VPL_CASE(2, W8A8_CALL_LN)
+    W8A8_VPL_CASE(4, W8A8_CALL_LN) W8A8_VPL_CASE(8, W8A8_CALL_LN)
+    W8A8_VPL_CASE(16, W8A8_CALL_LN)
+    default: break;
+  }
 #undef W8A8_CALL_LN
   return hipErrorInvalidValue;   // host validation rejects longer rows first
 }

@@ -22,6 +22,9 @@ The shapes and value distributions are those of the five workloads:
                 (21 latent frames x 30x52 tokens); W [5120,13824] ~N(0,0.01)
 * ``blockwise_small`` / ``blockwise_large``  X [1000 | 32760, 5120] ~N(0,1);
                 W [5120,5120] ~N(0,0.02)
+* ``ln_up_proj`` the up_proj shapes with a LayerNorm prologue instead of the
+                RMSNorm: no affine, eps 1e-6, adaLN modulation scale and shift
+                [4096] ~N(0,0.2); X ~N(0,1); W ~N(0,0.02)
 """
 from __future__ import annotations
 
@@ -31,7 +34,7 @@ import torch
 
 CHUNK_ROWS = 1024
 
-_TAGS = {"x": 1, "w": 2, "gamma": 3, "outlier": 4}
+_TAGS = {"x": 1, "w": 2, "gamma": 3, "outlier": 4, "mod_scale": 5, "mod_shift": 6}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -51,6 +54,8 @@ class Workload:
     gamma_std: float = 0.1
     eps: float = 1e-6
     blockwise: bool = False     # 1x128 activation / 128x128 weight scales
+    layernorm: bool = False     # LayerNorm + adaLN modulation prologue (no affine)
+    mod_std: float = 0.2
 
     @property
     def gemm_ops(self) -> int:
@@ -68,6 +73,8 @@ WORKLOADS = {
                                 1.0, 0.02, blockwise=True),
     "blockwise_large": Workload("blockwise_large", 32760, 5120, 5120, 1006, "normal",
                                 1.0, 0.02, blockwise=True),
+    "ln_up_proj": Workload("ln_up_proj", 28672, 16384, 4096, 1007, "normal", 1.0, 0.02,
+                           layernorm=True),
 }
 
 
@@ -130,6 +137,12 @@ def gamma_bits(wl: Workload) -> np.ndarray:
     """RMSNorm gain [K] ~ N(gamma_mean, gamma_std) as BF16 bits."""
     z = torch.randn(wl.K, generator=_gen(wl.seed, "gamma", 0), dtype=torch.float32)
     return _to_bf16_bits(z * wl.gamma_std + wl.gamma_mean)
+
+
+def mod_bits(wl: Workload, which: str) -> np.ndarray:
+    """adaLN modulation vector [K] ("mod_scale" or "mod_shift") ~ N(0, mod_std) as BF16 bits."""
+    z = torch.randn(wl.K, generator=_gen(wl.seed, which, 0), dtype=torch.float32)
+    return _to_bf16_bits(z * wl.mod_std)
 
 
 def random_bits(shape, seed: int, std: float = 1.0, mean: float = 0.0) -> np.ndarray:
