@@ -43,6 +43,10 @@ R11 LayerNorm prologue ("Turbodiffusion Video", "Custom Kernel Optimizations":
     arithmetic, z = bf16(fl32(bf16(fl32(y * m)) + shift)), m =
     bf16(fl32(1 + scale)), with per-channel scale and shift; then the
     per-token quantisation of z.
+R12 bias of an Int8Linear (next row f2: "Reused Components", W8A8 Linear
+    bullet, Int8Linear replaces Linear, which may carry a bias): added in fp32
+    after both scales, before the one BF16 rounding:
+    out = bf16(fl32(fl32(fl32(fl32(acc) * sa) * sw) + bias)).
 
 Floating-point values are BF16 bit patterns (uint16) at the interface.
 """
@@ -54,7 +58,7 @@ __all__ = [
     "QMAX", "BLOCK", "bf16_to_f32", "f32_to_bf16", "quantize_groups",
     "quantize_rows", "rmsnorm_inv_rms", "rmsnorm_bf16", "rmsnorm_quant",
     "layernorm_stats", "layernorm_bf16", "modulate_bf16", "layernorm_quant",
-    "gemm_i32", "postscale_bf16", "fma_f32", "gemm_blockwise_bf16",
+    "gemm_i32", "postscale_bf16", "postscale_bias_bf16", "fma_f32", "gemm_blockwise_bf16",
     "w8a8_linear", "check_gemm_shape", "ShapeError", "bf16_ulp_distance",
 ]
 
@@ -334,6 +338,20 @@ def postscale_bf16(acc: np.ndarray, sa: np.ndarray, sw: np.ndarray) -> np.ndarra
     return f32_to_bf16(v)
 
 
+def postscale_bias_bf16(acc: np.ndarray, sa: np.ndarray, sw: np.ndarray,
+                        bias_bits: np.ndarray) -> np.ndarray:
+    """out[m,n] = bf16(fl32(fl32(fl32(fl32(acc[m,n]) * sa[m]) * sw[n]) + bias[n])).
+
+    R12: an Int8Linear's bias joins the post-scale epilogue in fp32, so the
+    output is rounded to BF16 once, as a BF16 Linear with bias is.
+    """
+    a = np.asarray(acc, dtype=np.int32).astype(np.float32)
+    t = (a * np.asarray(sa, dtype=np.float32)[:, None]).astype(np.float32)
+    v = (t * np.asarray(sw, dtype=np.float32)[None, :]).astype(np.float32)
+    v = (v + bf16_to_f32(bias_bits)[None, :]).astype(np.float32)
+    return f32_to_bf16(v)
+
+
 # ---------------------------------------------------------------------------
 # Blockwise-scaled variant (R7)
 # ---------------------------------------------------------------------------
@@ -421,12 +439,14 @@ def check_gemm_shape(M: int, N: int, K: int) -> None:
         raise ShapeError("K too large for an INT32 accumulator")
 
 
-def w8a8_linear(x_bits: np.ndarray, w_bits: np.ndarray):
+def w8a8_linear(x_bits: np.ndarray, w_bits: np.ndarray, bias_bits: np.ndarray | None = None):
     """Whole W8A8 Linear: per-channel weight quant (init), per-token activation
-    quant (per call), exact INT32 GEMM, fp32 post-scale to BF16.
+    quant (per call), exact INT32 GEMM, fp32 post-scale (and bias, R12) to BF16.
     Returns (out_bits, qa, sa, qw, sw, acc)."""
     qw, sw = quantize_rows(w_bits)
     qa, sa = quantize_rows(x_bits)
     acc = gemm_i32(qa, qw)
-    return postscale_bf16(acc, sa, sw), qa, sa, qw, sw, acc
+    if bias_bits is None:
+        return postscale_bf16(acc, sa, sw), qa, sa, qw, sw, acc
+    return postscale_bias_bf16(acc, sa, sw, bias_bits), qa, sa, qw, sw, acc
 

@@ -401,6 +401,48 @@ def test_postscale_exact():
     assert check_postscale_pins(O.postscale_bf16)
 
 
+def check_postscale_bias_pins(post_fn) -> bool:
+    acc = W.random_int8((16, 16), 74).astype(np.int32) * 1_000_003
+    acc[0, 1] = 2**24 + 1
+    sa = W.random_scales((16,), 75)
+    sw = W.random_scales((16,), 76, lo=1e-5, hi=10.0)
+    bias = W.random_bits((16,), seed=77, std=0.5)
+    bias[3] = 0
+    out = post_fn(acc, sa, sw, bias)
+    for m in range(16):
+        for n in range(16):
+            a = Fraction(int(acc[m, n]))
+            s1, s2 = Fraction(float(sa[m])), Fraction(float(sw[n]))
+            want = E.bf16(E.f32(E.f32(E.f32(E.f32(a) * s1) * s2) + E.bf16_value(bias[n])))
+            if E.bf16_value(out[m, n]) != want:
+                return False
+    # a zero activation scale leaves exactly the bias; a zero bias the post-scale value
+    sa0 = sa.copy()
+    sa0[5] = 0
+    if not np.array_equal(O.bf16_to_f32(post_fn(acc, sa0, sw, bias)[5]), O.bf16_to_f32(bias)):
+        return False
+    zero = np.zeros(16, np.uint16)
+    return np.array_equal(O.bf16_to_f32(post_fn(acc, sa, sw, zero)),
+                          O.bf16_to_f32(O.postscale_bf16(acc, sa, sw)))
+
+
+def test_postscale_bias_exact():
+    assert check_postscale_bias_pins(O.postscale_bias_bf16)
+
+
+def test_w8a8_linear_bias_close_to_bf16_product():
+    """Informational bound: the W8A8 Linear with bias stays within quantisation
+    noise of torch's float64 Linear on the unquantised inputs."""
+    x = W.random_bits((32, 256), seed=78)
+    w = W.random_bits((128, 256), seed=79, std=0.02)
+    b = W.random_bits((128,), seed=80, std=0.1)
+    out, *_ = O.w8a8_linear(x, w, b)
+    ref = (O.bf16_to_f32(x).astype(np.float64) @ O.bf16_to_f32(w).astype(np.float64).T
+           + O.bf16_to_f32(b).astype(np.float64))
+    rel = np.linalg.norm(O.bf16_to_f32(out) - ref) / np.linalg.norm(ref)
+    assert rel < 0.02
+
+
 def test_postscale_special_cases():
     acc = np.arange(-256, 256, dtype=np.int32).reshape(2, 256)
     out = O.postscale_bf16(acc, np.ones(2, np.float32), np.ones(256, np.float32))
@@ -579,6 +621,22 @@ def _post_swapped_scales(acc, sa, sw):
     return O.postscale_bf16(acc, sw, sa)
 
 
+def _bias_before_weight_scale(acc, sa, sw, bias):
+    a = np.asarray(acc, np.int32).astype(np.float32)
+    t = (a * sa[:, None]).astype(np.float32)
+    t = (t + O.bf16_to_f32(bias)[None, :]).astype(np.float32)
+    return O.f32_to_bf16((t * sw[None, :]).astype(np.float32))
+
+
+def _bias_after_rounding(acc, sa, sw, bias):
+    y = O.bf16_to_f32(O.postscale_bf16(acc, sa, sw))
+    return O.f32_to_bf16((y + O.bf16_to_f32(bias)[None, :]).astype(np.float32))
+
+
+def _bias_by_row(acc, sa, sw, bias):
+    return O.postscale_bias_bf16(acc.T.copy(), sw, sa, bias).T.copy()
+
+
 def _bw_wrong_block_index(qa, sa, qw, sw):
     sw2 = np.roll(sw, 1, axis=0)
     return O.gemm_blockwise_bf16(qa, sa, qw, sw2)
@@ -602,3 +660,6 @@ def test_planted_mistakes():
     assert not check_postscale_pins(_post_dropped_weight_scale)
     assert not check_blockwise_pins(_bw_wrong_block_index)
     assert not check_blockwise_pins(_bw_descending)
+    assert not check_postscale_bias_pins(_bias_before_weight_scale)
+    assert not check_postscale_bias_pins(_bias_after_rounding)
+    assert not check_postscale_bias_pins(_bias_by_row)
