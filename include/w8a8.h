@@ -176,6 +176,24 @@ w8a8_status_t w8a8_gemm_postscale(const int8_t* a, int64_t lda, const int8_t* w,
                                   int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
+ * w8a8_gemm_postscale_bias -- w8a8_gemm_postscale with an Int8Linear's bias
+ * added in the epilogue.
+ *
+ * Passage: "Reused Components", W8A8 Linear bullet (Int8Linear takes the place
+ * of Linear, which may carry a bias), with the epilogue of w8a8_gemm_postscale.
+ *
+ *   out[m,n] = bf16(fl32(fl32(fl32(fl32(acc) * a_scale[m]) * w_scale[n]) + bias[n]))
+ *
+ *   bias  [N] BF16, 16-byte aligned (input)
+ * Everything else, requirements and errors as w8a8_gemm_postscale; the output
+ * must not overlap the bias either.
+ */
+w8a8_status_t w8a8_gemm_postscale_bias(const int8_t* a, int64_t lda, const int8_t* w,
+                                       int64_t ldw, const float* a_scale, const float* w_scale,
+                                       const uint16_t* bias, uint16_t* out, int64_t ldo,
+                                       int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * w8a8_gemm_blockwise -- blockwise-scaled W8A8 GEMM (the original
  * TurboDiffusion scheme, "Differences From TurboDiffusion", W8A8 kernel row).
  *

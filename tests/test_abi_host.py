@@ -35,7 +35,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"w8a8_quant_rows", "w8a8_rmsnorm_quant", "w8a8_layernorm_quant",
-                          "w8a8_gemm_postscale",
+                          "w8a8_gemm_postscale", "w8a8_gemm_postscale_bias",
                           "w8a8_gemm_blockwise", "w8a8_gemm_i32", "w8a8_status_string",
                           "w8a8_last_error", "w8a8_version"}
     raw = ctypes.CDLL(w8.LIB_PATH)
@@ -135,6 +135,8 @@ def test_layernorm_quant_optional_vectors_may_be_null():
 def gemm(fn="w8a8_gemm_postscale", a=P, lda=256, w=Q, ldw=256, sa=S, sw=S + 0x100000,
          out=O, ldo=128, M=64, N=128, K=256):
     f = getattr(w8.lib(), fn)
+    if fn == "w8a8_gemm_postscale_bias":
+        return f(a, lda, w, ldw, sa, sw, S + 0x200000, out, ldo, M, N, K, None)
     if fn == "w8a8_gemm_i32":
         return f(a, lda, w, ldw, out, ldo, M, N, K, None)
     return f(a, lda, w, ldw, sa, sw, out, ldo, M, N, K, None)
@@ -161,7 +163,8 @@ GEMM_CASES = [
 
 
 @pytest.mark.parametrize("kwargs,status", GEMM_CASES)
-@pytest.mark.parametrize("fn", ["w8a8_gemm_postscale", "w8a8_gemm_blockwise"])
+@pytest.mark.parametrize("fn", ["w8a8_gemm_postscale", "w8a8_gemm_postscale_bias",
+                                "w8a8_gemm_blockwise"])
 def test_gemm_rejects(fn, kwargs, status):
     assert gemm(fn, **kwargs) == status
 
@@ -176,6 +179,19 @@ def test_gemm_null_scales():
     assert gemm(sa=None) == INVALID
     assert gemm("w8a8_gemm_blockwise", sw=None) == INVALID
     assert gemm(sa=S + 2) == UNSUPPORTED
+
+
+def bias_gemm(bias, out=O, M=64, N=128):
+    return w8.lib().w8a8_gemm_postscale_bias(P, 256, Q, 256, S, S + 0x100000, bias, out, N,
+                                             M, N, 256, None)
+
+
+def test_gemm_bias_rejects():
+    assert bias_gemm(None) == INVALID
+    assert bias_gemm(S + 0x200008) == UNSUPPORTED                    # bias not 16-byte aligned
+    assert bias_gemm(O + 0x1000) == INVALID                          # bias inside the output
+    assert bias_gemm(O - 0x100, N=256) == INVALID                    # bias runs into the output
+    assert bias_gemm(None, M=0) == OK                                # empty call: a no-op
 
 
 def test_empty_calls_are_noops():
@@ -206,3 +222,12 @@ def test_binding_rejects_host_tensors():
     a = torch.zeros(4, 256, dtype=torch.int8)
     with pytest.raises(w8.W8A8Error):
         w8.w8a8_gemm_i32(a, a)
+
+
+def test_int8_linear_rejects_cpu_weights():
+    with pytest.raises(w8.W8A8Error):
+        w8.Int8Linear(torch.zeros(128, 256, dtype=torch.bfloat16))
+    assert w8.linear.int8_shape_supported(128, 256)
+    assert not w8.linear.int8_shape_supported(100, 256)
+    assert not w8.linear.int8_shape_supported(128, 200)
+    assert not w8.linear.int8_shape_supported(128, w8.W8A8_MAX_K + 128)

@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "W8A8Error", "W8A8Unsupported", "lib", "LIB_PATH", "EXPORTED_SYMBOLS",
     "w8a8_quant_rows", "w8a8_rmsnorm_quant", "w8a8_layernorm_quant", "w8a8_gemm_postscale",
-    "w8a8_gemm_blockwise", "w8a8_gemm_i32", "w8a8_version",
+    "w8a8_gemm_blockwise", "w8a8_gemm_i32", "w8a8_version", "Int8Linear",
+    "replace_linear_with_int8",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw8a8.so")
@@ -56,6 +57,7 @@ _SIGS = {
     "w8a8_layernorm_quant": [_p, _p, _p, _p, _p, ctypes.c_float, _i64, _i64, _i64, _p, _i64, _p,
                              _p, _p, _p],
     "w8a8_gemm_postscale": [_p, _i64, _p, _i64, _p, _p, _p, _i64, _i64, _i64, _i64, _p],
+    "w8a8_gemm_postscale_bias": [_p, _i64, _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p],
     "w8a8_gemm_blockwise": [_p, _i64, _p, _i64, _p, _p, _p, _i64, _i64, _i64, _i64, _p],
     "w8a8_gemm_i32": [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p],
 }
@@ -219,13 +221,22 @@ def _gemm_args(a, w, out, out_dtype):
 
 
 def w8a8_gemm_postscale(a: torch.Tensor, w: torch.Tensor, a_scale: torch.Tensor,
-                        w_scale: torch.Tensor, out: torch.Tensor | None = None, stream=None):
-    """out[M,N] (BF16) = bf16(acc * a_scale[m] * w_scale[n]), acc the exact
-    INT32 sum over K of a[m,k] * w[n,k]."""
+                        w_scale: torch.Tensor, out: torch.Tensor | None = None, stream=None,
+                        bias: torch.Tensor | None = None):
+    """out[M,N] (BF16) = bf16(acc * a_scale[m] * w_scale[n] (+ bias[n])), acc the
+    exact INT32 sum over K of a[m,k] * w[n,k]; with a bias this calls
+    w8a8_gemm_postscale_bias."""
     M, N, K, out = _gemm_args(a, w, out, torch.bfloat16)
-    st = _lib.w8a8_gemm_postscale(_ptr(a), _ld(a), _ptr(w), _ld(w), _ptr(a_scale), _ptr(w_scale),
-                                  _ptr(out), _ld(out), M, N, K, _stream(stream))
-    _check(st, "w8a8_gemm_postscale")
+    if bias is None:
+        st = _lib.w8a8_gemm_postscale(_ptr(a), _ld(a), _ptr(w), _ld(w), _ptr(a_scale),
+                                      _ptr(w_scale), _ptr(out), _ld(out), M, N, K, _stream(stream))
+        _check(st, "w8a8_gemm_postscale")
+        return out
+    _vec(bias, torch.bfloat16, N, "bias")
+    st = _lib.w8a8_gemm_postscale_bias(_ptr(a), _ld(a), _ptr(w), _ld(w), _ptr(a_scale),
+                                       _ptr(w_scale), _ptr(bias), _ptr(out), _ld(out), M, N, K,
+                                       _stream(stream))
+    _check(st, "w8a8_gemm_postscale_bias")
     return out
 
 
@@ -246,3 +257,6 @@ def w8a8_gemm_i32(a: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = N
                             _stream(stream))
     _check(st, "w8a8_gemm_i32")
     return out
+
+
+from .linear import Int8Linear, replace_linear_with_int8  # noqa: E402  (needs the binding above)

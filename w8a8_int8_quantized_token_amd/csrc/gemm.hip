@@ -11,13 +11,15 @@
 namespace w8a8 {
 
 hipError_t launch_gemm(Epilogue epi, const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
-                       const float* a_scale, const float* w_scale, void* out, int64_t ldo,
-                       int64_t M, int64_t N, int64_t K, hipStream_t st) {
+                       const float* a_scale, const float* w_scale, const uint16_t* bias,
+                       void* out, int64_t ldo, int64_t M, int64_t N, int64_t K, hipStream_t st) {
   if (M == 0) return hipSuccess;
   switch (epi) {
     case Epilogue::kPostscaleBf16:
+    case Epilogue::kPostscaleBiasBf16:
     case Epilogue::kInt32:
-      return launch_gemm_pipelined(epi, a, lda, w, ldw, a_scale, w_scale, out, ldo, M, N, K, st);
+      return launch_gemm_pipelined(epi, a, lda, w, ldw, a_scale, w_scale, bias, out, ldo, M, N, K,
+                                   st);
     case Epilogue::kBlockwiseBf16:
       return launch_gemm_blockwise(a, lda, w, ldw, a_scale, w_scale,
                                    reinterpret_cast<uint16_t*>(out), ldo, M, N, K, st);

@@ -46,8 +46,9 @@ constexpr int kTN = 8, kTM = 4;       // 16x16 MFMA tiles per wave: 128 channels
 constexpr int kLoads = (kBN + kBM) * kBK / 1024 / kWaves;   // 1 KiB wave-loads per stage: 8
 constexpr int kStoresPerTile = kTM * 4;                       // 16-byte stores per wave per tile
 constexpr int kScaleBytes = (kBN + kBM) * 4;   // one tile's scales
+constexpr int kBiasBytes = kWaves * 256;       // one dword wave-load per wave (the tile's
+                                               // 256 BF16 biases fill the first 512 bytes)
 constexpr int kScaleBufs = 3;                  // tile k's scales sit in buffer k % 3
-constexpr int kScaleLoads = 1;                 // scale wave-loads per wave per tile
 constexpr int kGroupM = 8;
 
 // 128-byte LDS rows hold 8 chunks of 16 bytes; logical chunk c of row r sits
@@ -72,11 +73,16 @@ template <Epilogue kEpi>
 __global__ __launch_bounds__(kThreads, 1)
 void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* __restrict__ w,
                        int64_t ldw, const float* __restrict__ a_scale,
-                       const float* __restrict__ w_scale, void* __restrict__ out, int64_t ldo,
-                       int M, int N, int K, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) int8_t lds[kSlots * kSlotBytes + kScaleBufs * kScaleBytes];
-  int8_t* const scale_bufs = lds + kSlots * kSlotBytes;
+                       const float* __restrict__ w_scale, const uint16_t* __restrict__ bias,
+                       void* __restrict__ out, int64_t ldo, int M, int N, int K, int tiles_m,
+                       int tiles_n) {
   constexpr bool kScales = kEpi != Epilogue::kInt32;
+  constexpr bool kBias = kEpi == Epilogue::kPostscaleBiasBf16;
+  // a tile's scales, then (with a bias) its biases
+  constexpr int kBufBytes = kScaleBytes + (kBias ? kBiasBytes : 0);
+  constexpr int kScaleLoads = kBias ? 2 : 1;   // wave-loads per wave per tile
+  __shared__ __attribute__((aligned(1024))) int8_t lds[kSlots * kSlotBytes + kScaleBufs * kBufBytes];
+  int8_t* const scale_bufs = lds + kSlots * kSlotBytes;
 
   const Sched sc = make_sched(blockIdx.x, gridDim.x, tiles_m, tiles_n);
   const int nk = K / kBK;                       // stages per tile
@@ -148,7 +154,7 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   auto issue_scales = [&](int k) {
     int m0, n0;
     tile_mn(sc, k, m0, n0);
-    int8_t* buf = scale_bufs + (k % kScaleBufs) * kScaleBytes;
+    int8_t* buf = scale_bufs + (k % kScaleBufs) * kBufBytes;
     // a buffer over the whole scale vector; indices past the end are clamped
     // to its last element (clamped rows reuse row M-1's scale). The lane
     // offset is recomputed here rather than kept live across the tile.
@@ -160,6 +166,17 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
         buffer_rsrc(wave < 4 ? w_scale : a_scale, (uint32_t)(4 * lim));
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + wave * 256), 4, 4 * idx, 0, 0,
                                              0);
+    if constexpr (kBias) {
+      // BF16 biases as dwords (pairs of channels): waves 0 and 1 bring the
+      // tile's 128 dwords, the other waves the same again into space nothing
+      // reads, so every wave issues the same loads
+      const int nd = N >> 1;
+      int di = (n0 >> 1) + 64 * (wave & 1) + ln;
+      di = di < nd ? di : nd - 1;
+      const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(bias, (uint32_t)(4 * nd));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(buf + kScaleBytes + wave * 256), 4,
+                                               4 * di, 0, 0, 0);
+    }
   };
 
   // ---- fragments: MFMA row slot ir = lane % 16 of W tile i maps to wave-local
@@ -215,7 +232,7 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
     } else {
       uint16_t* o = reinterpret_cast<uint16_t*>(out);
       // the tile's scales, brought into LDS one tile ahead
-      const uint32_t sbuf = lds_addr(scale_bufs + (k % kScaleBufs) * kScaleBytes);
+      const uint32_t sbuf = lds_addr(scale_bufs + (k % kScaleBufs) * kBufBytes);
       float sa[kTM];
 #pragma unroll
       for (int j = 0; j < kTM; ++j)
@@ -235,6 +252,18 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
                      : "memory");
         const float sw[2 * kTN] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3],
                                    t2[0], t2[1], t2[2], t2[3], t3[0], t3[1], t3[2], t3[3]};
+        // the lane's 16 biases of this half: channel c of the tile at 2 c
+        uint32_t bw[kBias ? 8 : 1];
+        if constexpr (kBias) {
+          const uint32_t ba = sbuf + kScaleBytes + 2 * (wn * 128 + 32 * kq + 16 * hf);
+          v4f b0 = lds_read_f4(ba), b1 = lds_read_f4(ba + 16);
+          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b0), "+v"(b1) : : "memory");
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bw[e] = __float_as_uint(b0[e]);
+            bw[4 + e] = __float_as_uint(b1[e]);
+          }
+        }
 #pragma unroll
         for (int j = 0; j < kTM; ++j) {
           // Rows past M hold exactly row M-1's sums (their loads were clamped
@@ -247,10 +276,16 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
 #pragma unroll
           for (int ii = 0; ii < kTN / 2; ++ii) {
             const int i = (kTN / 2) * hf + ii;
-            const float v0 = ((float)acc[i][j][0] * sa[j]) * sw[4 * ii + 0];
-            const float v1 = ((float)acc[i][j][1] * sa[j]) * sw[4 * ii + 1];
-            const float v2 = ((float)acc[i][j][2] * sa[j]) * sw[4 * ii + 2];
-            const float v3 = ((float)acc[i][j][3] * sa[j]) * sw[4 * ii + 3];
+            float v0 = ((float)acc[i][j][0] * sa[j]) * sw[4 * ii + 0];
+            float v1 = ((float)acc[i][j][1] * sa[j]) * sw[4 * ii + 1];
+            float v2 = ((float)acc[i][j][2] * sa[j]) * sw[4 * ii + 2];
+            float v3 = ((float)acc[i][j][3] * sa[j]) * sw[4 * ii + 3];
+            if constexpr (kBias) {   // channels 4 ii .. 4 ii + 3 of this half
+              v0 = v0 + bf16_lo(bw[2 * ii]);
+              v1 = v1 + bf16_hi(bw[2 * ii]);
+              v2 = v2 + bf16_lo(bw[2 * ii + 1]);
+              v3 = v3 + bf16_hi(bw[2 * ii + 1]);
+            }
             pk[2 * ii] = pack_bf16x2(v0, v1);
             pk[2 * ii + 1] = pack_bf16x2(v2, v3);
           }
@@ -352,22 +387,21 @@ int device_cu_count() {
 
 hipError_t launch_gemm_pipelined(Epilogue epi, const int8_t* a, int64_t lda, const int8_t* w,
                                  int64_t ldw, const float* a_scale, const float* w_scale,
-                                 void* out, int64_t ldo, int64_t M, int64_t N, int64_t K,
-                                 hipStream_t st) {
+                                 const uint16_t* bias, void* out, int64_t ldo, int64_t M,
+                                 int64_t N, int64_t K, hipStream_t st) {
   const int tiles_m = (int)((M + pipe::kBM - 1) / pipe::kBM);
   const int tiles_n = (int)((N + pipe::kBN - 1) / pipe::kBN);
   const int64_t tiles = (int64_t)tiles_m * tiles_n;
   const int cus = device_cu_count();
   const int grid = (int)(tiles < cus ? tiles : cus);
   const dim3 block(pipe::kThreads);
-  if (epi == Epilogue::kInt32)
-    hipLaunchKernelGGL((pipe::gemm_i8_pipelined<Epilogue::kInt32>), dim3(grid), block, 0, st, a,
-                       lda, w, ldw, a_scale, w_scale, out, ldo, (int)M, (int)N, (int)K, tiles_m,
-                       tiles_n);
-  else
-    hipLaunchKernelGGL((pipe::gemm_i8_pipelined<Epilogue::kPostscaleBf16>), dim3(grid), block, 0,
-                       st, a, lda, w, ldw, a_scale, w_scale, out, ldo, (int)M, (int)N, (int)K,
-                       tiles_m, tiles_n);
+#define W8A8_PIPE_LAUNCH(E)                                                                       \
+  hipLaunchKernelGGL((pipe::gemm_i8_pipelined<E>), dim3(grid), block, 0, st, a, lda, w, ldw, \
+                     a_scale, w_scale, bias, out, ldo, (int)M, (int)N, (int)K, tiles_m, tiles_n)
+  if (epi == Epilogue::kInt32) W8A8_PIPE_LAUNCH(Epilogue::kInt32);
+  else if (epi == Epilogue::kPostscaleBiasBf16) W8A8_PIPE_LAUNCH(Epilogue::kPostscaleBiasBf16);
+  else W8A8_PIPE_LAUNCH(Epilogue::kPostscaleBf16);
+#undef W8A8_PIPE_LAUNCH
   return hipGetLastError();
 }
 

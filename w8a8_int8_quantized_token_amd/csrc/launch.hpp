@@ -27,7 +27,7 @@ hipError_t launch_layernorm_quant(const uint16_t* x, const uint16_t* gamma, cons
                                   int64_t rows, int64_t cols, int64_t ldx, int8_t* q, int64_t ldq,
                                   float* scale, float* mean, float* rstd, hipStream_t st);
 
-enum class Epilogue { kPostscaleBf16, kInt32, kBlockwiseBf16 };
+enum class Epilogue { kPostscaleBf16, kInt32, kBlockwiseBf16, kPostscaleBiasBf16 };
 
 // Compute units of the current device (cached per device); persistent grids
 // launch at most one workgroup per CU.
@@ -36,16 +36,17 @@ int device_cu_count();
 // Persistent pipelined kernel (post-scale and INT32 epilogues).
 hipError_t launch_gemm_pipelined(Epilogue epi, const int8_t* a, int64_t lda, const int8_t* w,
                                  int64_t ldw, const float* a_scale, const float* w_scale,
-                                 void* out, int64_t ldo, int64_t M, int64_t N, int64_t K,
-                                 hipStream_t st);
+                                 const uint16_t* bias, void* out, int64_t ldo, int64_t M,
+                                 int64_t N, int64_t K, hipStream_t st);
 
 // Persistent pipelined kernel with per-K-block scales.
 hipError_t launch_gemm_blockwise(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
                                  const float* a_scale, const float* w_scale, uint16_t* out,
                                  int64_t ldo, int64_t M, int64_t N, int64_t K, hipStream_t st);
 
+// bias (BF16 [N]) is read by the kPostscaleBiasBf16 epilogue only.
 hipError_t launch_gemm(Epilogue epi, const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
-                       const float* a_scale, const float* w_scale, void* out, int64_t ldo,
-                       int64_t M, int64_t N, int64_t K, hipStream_t st);
+                       const float* a_scale, const float* w_scale, const uint16_t* bias,
+                       void* out, int64_t ldo, int64_t M, int64_t N, int64_t K, hipStream_t st);
 
 }  // namespace w8a8

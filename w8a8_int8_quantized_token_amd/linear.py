@@ -1,0 +1,92 @@
+"""Int8Linear: the W8A8 Linear as a torch module.
+
+"TurboDiffusion Integration Notes", section "Reused Components", W8A8 Linear
+bullet: selected Linear layers become INT8 once, when the model is set up,
+their activations are quantised dynamically before every call, and shapes the
+INT8 kernels do not cover keep using the native Linear. The module therefore
+keeps the BF16 weight (for those shapes), quantises it per output channel once
+at construction, and on every call quantises the activation per token and runs
+the INT8 GEMM with the scales (and the bias) applied in its epilogue.
+
+Every INT8 step is a call into libw8a8; when the library reports
+W8A8_ERR_UNSUPPORTED_SHAPE the call runs torch's BF16 Linear on the same
+device instead. There is no CPU path: CPU tensors are an error.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import W8A8Error, W8A8Unsupported, W8A8_ERR_INVALID_ARGUMENT, W8A8_MAX_K
+from . import w8a8_gemm_postscale, w8a8_quant_rows
+
+
+def int8_shape_supported(out_features: int, in_features: int) -> bool:
+    """Whether the INT8 GEMM takes a [out_features, in_features] weight: K a
+    multiple of 128 up to W8A8_MAX_K, N a multiple of 128."""
+    return (in_features % 128 == 0 and 128 <= in_features <= W8A8_MAX_K
+            and out_features % 128 == 0 and out_features > 0)
+
+
+class Int8Linear(torch.nn.Module):
+    """y = x W^T (+ b) with W quantised per output channel at construction and
+    x quantised per token on every call (BF16 in, BF16 out)."""
+
+    def __init__(self, weight: torch.Tensor, bias: torch.Tensor | None = None):
+        super().__init__()
+        if not isinstance(weight, torch.Tensor) or weight.device.type != "cuda":
+            raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, "Int8Linear needs a weight on a GPU")
+        weight = weight.detach().to(torch.bfloat16).contiguous()
+        self.out_features, self.in_features = weight.shape
+        self.register_buffer("weight", weight)
+        self.register_buffer("bias", None if bias is None else
+                             bias.detach().to(device=weight.device, dtype=torch.bfloat16)
+                             .contiguous())
+        self.int8 = int8_shape_supported(self.out_features, self.in_features)
+        qw = sw = None
+        if self.int8:
+            try:
+                qw, sw = w8a8_quant_rows(weight)
+            except W8A8Unsupported:
+                self.int8 = False
+        self.register_buffer("qweight", qw)
+        self.register_buffer("weight_scale", sw)
+
+    @classmethod
+    def from_linear(cls, linear: torch.nn.Linear) -> "Int8Linear":
+        return cls(linear.weight, linear.bias)
+
+    def extra_repr(self) -> str:
+        return (f"in_features={self.in_features}, out_features={self.out_features}, "
+                f"bias={self.bias is not None}, int8={self.int8}")
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if x.device.type != "cuda":
+            raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, "Int8Linear runs on the GPU only")
+        if x.dtype != torch.bfloat16:
+            raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, "Int8Linear takes BF16 activations")
+        if self.int8:
+            x2 = x.reshape(-1, self.in_features)
+            if not x2.is_contiguous():
+                x2 = x2.contiguous()
+            try:
+                qa, sa = w8a8_quant_rows(x2)
+                out = w8a8_gemm_postscale(qa, self.qweight, sa, self.weight_scale,
+                                          bias=self.bias)
+                return out.reshape(*x.shape[:-1], self.out_features)
+            except W8A8Unsupported:
+                pass
+        return torch.nn.functional.linear(x, self.weight, self.bias)
+
+
+def replace_linear_with_int8(module: torch.nn.Module, select=None) -> int:
+    """Swap the nn.Linear layers under `module` (those `select(name, layer)`
+    accepts, all by default) for Int8Linear, in place. Returns how many were
+    swapped. This is the model-side switch that turns the W8A8 path on."""
+    count = 0
+    for name, child in list(module.named_children()):
+        if isinstance(child, torch.nn.Linear) and (select is None or select(name, child)):
+            setattr(module, name, Int8Linear.from_linear(child))
+            count += 1
+        else:
+            count += replace_linear_with_int8(child, select)
+    return count
