@@ -260,7 +260,9 @@ GEMM_SHAPES = [((64, 128, 256), 51), ((1, 128, 128), 52), ((1000, 384, 512), 53)
                ((257, 640, 1024), 54), ((4096, 4096, 4096), 55), ((129, 5120, 13824), 56),
                ((300, 256, 128), 57), ((513, 1152, 640), 58),
                # more tiles than CUs: several tiles per persistent workgroup
-               ((4096, 16384, 256), 59), ((8292, 4096, 128), 60), ((2000, 3200, 384), 66)]
+               ((4096, 16384, 256), 59), ((8292, 4096, 128), 60), ((2000, 3200, 384), 66),
+               # one whole tile; one row short of it (clamped loads)
+               ((256, 256, 256), 80), ((255, 4096, 512), 81)]
 
 
 @pytest.mark.parametrize("shape,seed", GEMM_SHAPES)

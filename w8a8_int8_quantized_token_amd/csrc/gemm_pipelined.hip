@@ -24,9 +24,16 @@
 //    to back: the next tile's first stages are in flight during an epilogue.
 //    Workgroup b sits on XCD b % 8; each XCD owns a contiguous, M-grouped
 //    range of tiles so shared rows stay in that XCD's L2.
-//  * Weight rows are the MFMA "A" operand with permuted row slots so each
-//    lane ends up with 32 consecutive output channels of one token: the
-//    epilogue writes 64 contiguous bytes per token per lane.
+//  * Weight rows are the MFMA "A" operand with permuted row slots: per
+//    16-byte store, the four lanes of a token hold 32 consecutive output
+//    channels, so one store instruction writes 16 tokens x 64 contiguous
+//    bytes (16-byte pieces scattered over twice as many lines cost the
+//    epilogue about 40% more time).
+//  * With M and N of at least one tile, the last tile row and column are
+//    moved back to end at M and N (they overlap their neighbours, whose
+//    rows they recompute and store again with identical values), so every
+//    load is in range and its offset is a lane constant plus a scalar. Below
+//    that, rows past M or N load the last valid row instead.
 //  * LDS rows are XOR-swizzled in 16-byte chunks. A ds_read_b128 is served
 //    16 lanes at a time and is conflict-free when those lanes hit 16
 //    distinct 16-byte slots of the 256-byte bank line; the keys below give
@@ -52,13 +59,21 @@ constexpr int kScaleBufs = 3;                  // tile k's scales sit in buffer 
 constexpr int kGroupM = 8;
 
 // 128-byte LDS rows hold 8 chunks of 16 bytes; logical chunk c of row r sits
-// at c ^ key(r). Weight rows are read in the permuted slot order (rows r..r+3
-// and r+32..r+35 side by side), activation rows in order.
-__device__ __forceinline__ int key_w(int r) { return (r & 3) | (((r >> 5) & 1) << 2); }
+// at c ^ key(r). Weight rows are read in the permuted slot order (row slot
+// 4 q + e of tile i is row 32 (i / 2) + 8 q + 4 (i % 2) + e), activation rows
+// in order.
+__device__ __forceinline__ int key_w(int r) { return (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 1); }
 __device__ __forceinline__ int key_a(int r) { return r & 7; }
 
-__device__ __forceinline__ void tile_mn(const Sched& s, int k, int& m0, int& n0) {
+// Tile k's origin. In full-tile mode the last tile row and column end at M
+// and N.
+template <bool kFull>
+__device__ __forceinline__ void tile_mn(const Sched& s, int k, int& m0, int& n0, int M, int N) {
   tile_mn<kBM, kBN, kGroupM>(s, k, m0, n0);
+  if constexpr (kFull) {
+    m0 = m0 < M - kBM ? m0 : M - kBM;
+    n0 = n0 < N - kBN ? n0 : N - kBN;
+  }
 }
 
 __device__ __forceinline__ void mfma_all(v4i (&acc)[kTN][kTM], const v4i (&f)[kTN + kTM]) {
@@ -69,7 +84,7 @@ __device__ __forceinline__ void mfma_all(v4i (&acc)[kTN][kTM], const v4i (&f)[kT
       acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f[i], f[kTN + j], acc[i][j], 0, 0, 0);
 }
 
-template <Epilogue kEpi>
+template <Epilogue kEpi, bool kFull>
 __global__ __launch_bounds__(kThreads, 1)
 void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* __restrict__ w,
                        int64_t ldw, const float* __restrict__ a_scale,
@@ -99,15 +114,17 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   const int r_l = 8 * wave + (lane >> 3);
   const int p = lane & 7;
   const int cw = (p ^ key_w(r_l)) << 4, ca = (p ^ key_a(r_l)) << 4;
-  // The tile's weight and activation row blocks as buffers. Rows past N or M
-  // are clamped to the last valid row (their sums duplicate it and are stored
-  // over it with identical values). Lane offsets take two 32-bit operations
-  // per load; a stage adds its K offset in an SGPR.
+  // The tile's weight and activation row blocks as buffers. Full tiles: a
+  // load's offset is the lane's row-0 offset plus 64 g rows and the stage's
+  // K offset, both in an SGPR. Otherwise rows past N or M are clamped to the
+  // last valid row (their sums duplicate it and are stored over it with
+  // identical values).
   int ld_k = 0, ld_kt = 0, ld_rvn = 0, ld_rvm = 0;
+  const int vo_w = r_l * (int)ldw + cw, vo_a = r_l * (int)lda + ca;
   __amdgpu_buffer_rsrc_t ld_w, ld_a;
   auto load_tile = [&](int k) {
     int m0, n0;
-    tile_mn(sc, k, m0, n0);
+    tile_mn<kFull>(sc, k, m0, n0, M, N);
     const int rn = (N - n0) < kBN ? (N - n0) : kBN;
     const int rm = (M - m0) < kBM ? (M - m0) : kBM;
     ld_rvn = rn - 1;
@@ -122,17 +139,26 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
 #pragma unroll
     for (int g = 0; g < kLoads / 2; ++g) {
       const int r = r_l + 64 * g;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_w, (lds_void*)(dst + g * kWaves * 1024), 16,
-                                               (r < ld_rvn ? r : ld_rvn) * (int)ldw + cw, koff,
-                                               0, 0);
+      if constexpr (kFull)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_w, (lds_void*)(dst + g * kWaves * 1024), 16,
+                                                 vo_w, koff + 64 * g * (int)ldw, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_w, (lds_void*)(dst + g * kWaves * 1024), 16,
+                                                 (r < ld_rvn ? r : ld_rvn) * (int)ldw + cw, koff,
+                                                 0, 0);
     }
 #pragma unroll
     for (int g = 0; g < kLoads / 2; ++g) {
       const int r = r_l + 64 * g;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_a,
-                                               (lds_void*)(dst + kBN * kBK + g * kWaves * 1024),
-                                               16, (r < ld_rvm ? r : ld_rvm) * (int)lda + ca,
-                                               koff, 0, 0);
+      if constexpr (kFull)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_a,
+                                                 (lds_void*)(dst + kBN * kBK + g * kWaves * 1024),
+                                                 16, vo_a, koff + 64 * g * (int)lda, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_a,
+                                                 (lds_void*)(dst + kBN * kBK + g * kWaves * 1024),
+                                                 16, (r < ld_rvm ? r : ld_rvm) * (int)lda + ca,
+                                                 koff, 0, 0);
     }
   };
   // Loader advance. It branches, so it runs at the top of a stage: placed after
@@ -153,7 +179,7 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   // finished before a barrier of tile k - 1.
   auto issue_scales = [&](int k) {
     int m0, n0;
-    tile_mn(sc, k, m0, n0);
+    tile_mn<kFull>(sc, k, m0, n0, M, N);
     int8_t* buf = scale_bufs + (k % kScaleBufs) * kBufBytes;
     // a buffer over the whole scale vector; indices past the end are clamped
     // to its last element (clamped rows reuse row M-1's scale). The lane
@@ -180,10 +206,12 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   };
 
   // ---- fragments: MFMA row slot ir = lane % 16 of W tile i maps to wave-local
-  // channel 32 (ir / 4) + 4 i + ir % 4, so lane (ir, kq) ends up holding the 32
-  // consecutive channels 32 kq .. 32 kq + 31 of token ir + 16 j.
+  // channel 32 (i / 2) + 8 (ir / 4) + 4 (i % 2) + ir % 4, so lane (ir, kq)
+  // holds channels 32 p + 8 kq .. 32 p + 8 kq + 7 of token ir + 16 j in tiles
+  // 2 p and 2 p + 1 (p < 4): the four lanes of a token cover 32 consecutive
+  // channels.
   const int ir = lane & 15, kq = lane >> 4;
-  const int w_row0 = wn * 128 + 32 * (ir >> 2) + (ir & 3);
+  const int w_row0 = wn * 128 + 8 * (ir >> 2) + (ir & 3);
   const int a_row0 = kBN + wm * (16 * kTM) + ir;
   const int w_base = w_row0 * kBK, w_key = key_w(w_row0);
   const int a_base = a_row0 * kBK, a_key = key_a(a_row0 - kBN);
@@ -192,7 +220,8 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
     const int cl = ks * 4 + kq;
     const int wo = w_base + ((cl ^ w_key) << 4), ao = a_base + ((cl ^ a_key) << 4);
 #pragma unroll
-    for (int i = 0; i < kTN; ++i) f[i] = *reinterpret_cast<const v4i*>(sb + wo + i * 4 * kBK);
+    for (int i = 0; i < kTN; ++i)
+      f[i] = *reinterpret_cast<const v4i*>(sb + wo + (32 * (i >> 1) + 4 * (i & 1)) * kBK);
 #pragma unroll
     for (int j = 0; j < kTM; ++j)
       f[kTN + j] = *reinterpret_cast<const v4i*>(sb + ao + j * 16 * kBK);
@@ -214,20 +243,21 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
     const int el = lane_id();
     const int ir = el & 15, kq = el >> 4;
     int m0, n0;
-    tile_mn(sc, k, m0, n0);
+    tile_mn<kFull>(sc, k, m0, n0, M, N);
     const int n_wave = n0 + wn * 128;
     if (n_wave >= N) return;
-    const int n_lane = n_wave + 32 * kq;
+    const int n_lane = n_wave + 8 * kq;
     const int m_lane = m0 + wm * (16 * kTM) + ir;
     if constexpr (kEpi == Epilogue::kInt32) {
       int32_t* o = reinterpret_cast<int32_t*>(out);
 #pragma unroll
       for (int j = 0; j < kTM; ++j) {
         int m = m_lane + 16 * j;
-        m = m < M ? m : M - 1;      // clamped rows hold row M-1's sums
+        if constexpr (!kFull) m = m < M ? m : M - 1;   // clamped rows hold row M-1's sums
         int32_t* dst = o + (int64_t)m * ldo + n_lane;
 #pragma unroll
-        for (int i = 0; i < kTN; ++i) *reinterpret_cast<v4i*>(dst + 4 * i) = acc[i][j];
+        for (int i = 0; i < kTN; ++i)
+          *reinterpret_cast<v4i*>(dst + 32 * (i >> 1) + 4 * (i & 1)) = acc[i][j];
       }
     } else {
       uint16_t* o = reinterpret_cast<uint16_t*>(out);
@@ -238,25 +268,24 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
       for (int j = 0; j < kTM; ++j)
         sa[j] = lds_read_f1(sbuf + 4 * (kBN + wm * (16 * kTM) + 16 * j + ir));
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {          // two halves of 16 channels
-        static_assert(2 * kTN == 16, "four vectors of weight scales per half");
-        v4f t0 = lds_read_f4(sbuf + 4 * (wn * 128 + 32 * kq + 16 * hf));
-        v4f t1 = lds_read_f4(sbuf + 4 * (wn * 128 + 32 * kq + 16 * hf + 4));
-        v4f t2 = lds_read_f4(sbuf + 4 * (wn * 128 + 32 * kq + 16 * hf + 8));
-        v4f t3 = lds_read_f4(sbuf + 4 * (wn * 128 + 32 * kq + 16 * hf + 12));
-        // the wait names the loaded registers, so no use moves above it
+      for (int hf = 0; hf < 2; ++hf) {          // stores p = 2 hf and 2 hf + 1
+        // channels 32 p + 8 kq + e (e < 8) of the wave's 128
+        const uint32_t swa = sbuf + 4 * (wn * 128 + 64 * hf + 8 * kq);
+        v4f t0 = lds_read_f4(swa);
+        v4f t1 = lds_read_f4(swa + 16);
+        v4f t2 = lds_read_f4(swa + 128);
+        v4f t3 = lds_read_f4(swa + 144);
         asm volatile("s_waitcnt lgkmcnt(0)"
                      : "+v"(t0), "+v"(t1), "+v"(t2), "+v"(t3), "+v"(sa[0]), "+v"(sa[1]),
                        "+v"(sa[2]), "+v"(sa[3])
                      :
                      : "memory");
-        const float sw[2 * kTN] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3],
-                                   t2[0], t2[1], t2[2], t2[3], t3[0], t3[1], t3[2], t3[3]};
-        // the lane's 16 biases of this half: channel c of the tile at 2 c
+        const float sw[16] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3],
+                              t2[0], t2[1], t2[2], t2[3], t3[0], t3[1], t3[2], t3[3]};
         uint32_t bw[kBias ? 8 : 1];
         if constexpr (kBias) {
-          const uint32_t ba = sbuf + kScaleBytes + 2 * (wn * 128 + 32 * kq + 16 * hf);
-          v4f b0 = lds_read_f4(ba), b1 = lds_read_f4(ba + 16);
+          const uint32_t ba = sbuf + kScaleBytes + 2 * (wn * 128 + 64 * hf + 8 * kq);
+          v4f b0 = lds_read_f4(ba), b1 = lds_read_f4(ba + 64);
           asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b0), "+v"(b1) : : "memory");
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -266,32 +295,30 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
         }
 #pragma unroll
         for (int j = 0; j < kTM; ++j) {
-          // Rows past M hold exactly row M-1's sums (their loads were clamped
-          // to it) and its scale, so they store row M-1's values to row M-1:
-          // every lane issues its stores and the per-tile store count stays
-          // fixed.
+          // Rows past M (clamped tiles only) hold exactly row M-1's sums
+          // (their loads were clamped to it) and its scale, so they store row
+          // M-1's values to row M-1: every lane issues its stores and the
+          // per-tile store count stays fixed.
           int m = m_lane + 16 * j;
-          m = m < M ? m : M - 1;
-          uint32_t pk[kTN];
+          if constexpr (!kFull) m = m < M ? m : M - 1;
 #pragma unroll
-          for (int ii = 0; ii < kTN / 2; ++ii) {
-            const int i = (kTN / 2) * hf + ii;
-            float v0 = ((float)acc[i][j][0] * sa[j]) * sw[4 * ii + 0];
-            float v1 = ((float)acc[i][j][1] * sa[j]) * sw[4 * ii + 1];
-            float v2 = ((float)acc[i][j][2] * sa[j]) * sw[4 * ii + 2];
-            float v3 = ((float)acc[i][j][3] * sa[j]) * sw[4 * ii + 3];
-            if constexpr (kBias) {   // channels 4 ii .. 4 ii + 3 of this half
-              v0 = v0 + bf16_lo(bw[2 * ii]);
-              v1 = v1 + bf16_hi(bw[2 * ii]);
-              v2 = v2 + bf16_lo(bw[2 * ii + 1]);
-              v3 = v3 + bf16_hi(bw[2 * ii + 1]);
+          for (int pp = 0; pp < 2; ++pp) {
+            const int p = 2 * hf + pp;
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              v[e] = ((float)acc[2 * p + (e >> 2)][j][e & 3] * sa[j]) * sw[8 * pp + e];
+            if constexpr (kBias) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                v[2 * q] = v[2 * q] + bf16_lo(bw[4 * pp + q]);
+                v[2 * q + 1] = v[2 * q + 1] + bf16_hi(bw[4 * pp + q]);
+              }
             }
-            pk[2 * ii] = pack_bf16x2(v0, v1);
-            pk[2 * ii + 1] = pack_bf16x2(v2, v3);
+            uint16_t* dst = o + (int64_t)m * ldo + n_lane + 32 * p;
+            *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                        pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
           }
-          uint16_t* dst = o + (int64_t)m * ldo + n_lane + 16 * hf;
-          *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-          *reinterpret_cast<uint4*>(dst + 8) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
         }
       }
     }
@@ -300,9 +327,10 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   // The tile-start group (the previous tile's stores, then the next tile's
   // scale loads) goes out after the loads of the tile's second stage, so only
   // the tile's first barrier leaves it outstanding. Stores are counted only
-  // when every wave stores a full tile (N a multiple of 256); otherwise the
-  // wait covers them too, which is merely slower.
-  const int stores_per_tile = (kEpi != Epilogue::kInt32 && N % kBN == 0) ? kStoresPerTile : 0;
+  // when every wave stores a full tile (full-tile mode, or N a multiple of
+  // 256); otherwise the wait covers them too, which is merely slower.
+  const int stores_per_tile =
+      (kEpi != Epilogue::kInt32 && (kFull || N % kBN == 0)) ? kStoresPerTile : 0;
   int pending_stores = 0;
 
   // ---- prologue: tile 0's scales; stages 0 and 1 in flight; fragments of
@@ -395,12 +423,19 @@ hipError_t launch_gemm_pipelined(Epilogue epi, const int8_t* a, int64_t lda, con
   const int cus = device_cu_count();
   const int grid = (int)(tiles < cus ? tiles : cus);
   const dim3 block(pipe::kThreads);
-#define W8A8_PIPE_LAUNCH(E)                                                                       \
-  hipLaunchKernelGGL((pipe::gemm_i8_pipelined<E>), dim3(grid), block, 0, st, a, lda, w, ldw, \
-                     a_scale, w_scale, bias, out, ldo, (int)M, (int)N, (int)K, tiles_m, tiles_n)
-  if (epi == Epilogue::kInt32) W8A8_PIPE_LAUNCH(Epilogue::kInt32);
-  else if (epi == Epilogue::kPostscaleBiasBf16) W8A8_PIPE_LAUNCH(Epilogue::kPostscaleBiasBf16);
-  else W8A8_PIPE_LAUNCH(Epilogue::kPostscaleBf16);
+  // full-tile mode needs at least one whole tile in each direction
+  const bool full = M >= pipe::kBM && N >= pipe::kBN;
+#define W8A8_PIPE_LAUNCH(E, F)                                                           \
+  hipLaunchKernelGGL((pipe::gemm_i8_pipelined<E, F>), dim3(grid), block, 0, st, a, lda, w, \
+                     ldw, a_scale, w_scale, bias, out, ldo, (int)M, (int)N, (int)K, tiles_m,  \
+                     tiles_n)
+#define W8A8_PIPE_LAUNCH2(E)           \
+  if (full) W8A8_PIPE_LAUNCH(E, true); \
+  else W8A8_PIPE_LAUNCH(E, false)
+  if (epi == Epilogue::kInt32) { W8A8_PIPE_LAUNCH2(Epilogue::kInt32); }
+  else if (epi == Epilogue::kPostscaleBiasBf16) { W8A8_PIPE_LAUNCH2(Epilogue::kPostscaleBiasBf16); }
+  else { W8A8_PIPE_LAUNCH2(Epilogue::kPostscaleBf16); }
+#undef W8A8_PIPE_LAUNCH2
 #undef W8A8_PIPE_LAUNCH
   return hipGetLastError();
 }
