@@ -28,7 +28,8 @@
 //    16-byte store, the four lanes of a token hold 32 consecutive output
 //    channels, so one store instruction writes 16 tokens x 64 contiguous
 //    bytes (16-byte pieces scattered over twice as many lines cost the
-//    epilogue about 40% more time).
+//    epilogue about 40% more time). The stores are non-temporal; with the
+//    scattered pieces that was slower, with whole 64-byte runs it is faster.
 //  * With M and N of at least one tile, the last tile row and column are
 //    moved back to end at M and N (they overlap their neighbours, whose
 //    rows they recompute and store again with identical values), so every
@@ -315,9 +316,13 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
                 v[2 * q + 1] = v[2 * q + 1] + bf16_hi(bw[4 * pp + q]);
               }
             }
+            // Non-temporal: the output streams past the caches instead of
+            // evicting the activation and weight rows the next tiles read.
             uint16_t* dst = o + (int64_t)m * ldo + n_lane + 32 * p;
-            *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                                        pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+            __builtin_nontemporal_store(
+                v4u{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                    pack_bf16x2(v[6], v[7])},
+                reinterpret_cast<v4u*>(dst));
           }
         }
       }
