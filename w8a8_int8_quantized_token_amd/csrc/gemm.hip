@@ -4,8 +4,8 @@
 // TurboDiffusion", W8A8-kernel row and the paragraph under the table: the
 // post-scale kernel keeps one INT32 accumulation over all of K and applies the
 // activation and weight scales only in the epilogue (gemm_pipelined.hip; the
-// INT32 export shares its main loop); the original TurboDiffusion kernel
-// rescales per K block (gemm_blockwise.hip).
+// INT32 export shares its main loop; split-K for small grids in splitk.hip);
+// the original TurboDiffusion kernel rescales per K block (gemm_blockwise.hip).
 #include "launch.hpp"
 
 namespace w8a8 {
@@ -16,7 +16,30 @@ hipError_t launch_gemm(Epilogue epi, const int8_t* a, int64_t lda, const int8_t*
   if (M == 0) return hipSuccess;
   switch (epi) {
     case Epilogue::kPostscaleBf16:
-    case Epilogue::kPostscaleBiasBf16:
+    case Epilogue::kPostscaleBiasBf16: {
+      // Too few tiles to fill the chip: K in parts, INT32 partial sums in a
+      // stream-ordered workspace, then one pass that adds them and applies
+      // the epilogue (bit-identical to the single pass). If the workspace
+      // cannot be had, the single pass runs instead.
+      const int parts = splitk_parts(M, N, K, device_cu_count());
+      if (parts > 1) {
+        void* ws = nullptr;
+        if (hipMallocAsync(&ws, (size_t)parts * M * N * 4, st) == hipSuccess) {
+          hipError_t e = launch_gemm_pipelined(Epilogue::kInt32, a, lda, w, ldw, nullptr, nullptr,
+                                               nullptr, ws, N, M, N, K, st, parts);
+          if (e == hipSuccess)
+            e = launch_splitk_postscale(
+                static_cast<const int32_t*>(ws), parts, M, N, a_scale, w_scale,
+                epi == Epilogue::kPostscaleBiasBf16 ? bias : nullptr,
+                reinterpret_cast<uint16_t*>(out), ldo, st);
+          const hipError_t f = hipFreeAsync(ws, st);
+          return e != hipSuccess ? e : f;
+        }
+        (void)hipGetLastError();   // the failed allocation is not the caller's error
+      }
+      return launch_gemm_pipelined(epi, a, lda, w, ldw, a_scale, w_scale, bias, out, ldo, M, N, K,
+                                   st);
+    }
     case Epilogue::kInt32:
       return launch_gemm_pipelined(epi, a, lda, w, ldw, a_scale, w_scale, bias, out, ldo, M, N, K,
                                    st);

@@ -66,15 +66,26 @@ constexpr int kGroupM = 8;
 __device__ __forceinline__ int key_w(int r) { return (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 1); }
 __device__ __forceinline__ int key_a(int r) { return r & 7; }
 
-// Tile k's origin. In full-tile mode the last tile row and column end at M
-// and N.
+// A workgroup's k-th item: its tile origin (in full-tile mode the last tile
+// row and column end at M and N) and, for a GEMM split over K into `splits`
+// parts, its part and that part's stages kb0 .. kb0 + kbn - 1 of the nk.
+struct Item {
+  int m0, n0, part, kb0, kbn;
+};
 template <bool kFull>
-__device__ __forceinline__ void tile_mn(const Sched& s, int k, int& m0, int& n0, int M, int N) {
-  tile_mn<kBM, kBN, kGroupM>(s, k, m0, n0);
+__device__ __forceinline__ Item item_of(const Sched& s, int k, int M, int N, int nk, int splits) {
+  Item it;
+  const int id = s.start + k * s.stride;
+  const int T = s.tiles_m * s.tiles_n;
+  it.part = splits == 1 ? 0 : id / T;
+  tile_of<kBM, kBN, kGroupM>(s, id - it.part * T, it.m0, it.n0);
   if constexpr (kFull) {
-    m0 = m0 < M - kBM ? m0 : M - kBM;
-    n0 = n0 < N - kBN ? n0 : N - kBN;
+    it.m0 = it.m0 < M - kBM ? it.m0 : M - kBM;
+    it.n0 = it.n0 < N - kBN ? it.n0 : N - kBN;
   }
+  it.kb0 = it.part * nk / splits;
+  it.kbn = (it.part + 1) * nk / splits - it.kb0;
+  return it;
 }
 
 __device__ __forceinline__ void mfma_all(v4i (&acc)[kTN][kTM], const v4i (&f)[kTN + kTM]) {
@@ -91,7 +102,7 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
                        int64_t ldw, const float* __restrict__ a_scale,
                        const float* __restrict__ w_scale, const uint16_t* __restrict__ bias,
                        void* __restrict__ out, int64_t ldo, int M, int N, int K, int tiles_m,
-                       int tiles_n) {
+                       int tiles_n, int splits) {
   constexpr bool kScales = kEpi != Epilogue::kInt32;
   constexpr bool kBias = kEpi == Epilogue::kPostscaleBiasBf16;
   // a tile's scales, then (with a bias) its biases
@@ -100,10 +111,11 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   __shared__ __attribute__((aligned(1024))) int8_t lds[kSlots * kSlotBytes + kScaleBufs * kBufBytes];
   int8_t* const scale_bufs = lds + kSlots * kSlotBytes;
 
-  const Sched sc = make_sched(blockIdx.x, gridDim.x, tiles_m, tiles_n);
-  const int nk = K / kBK;                       // stages per tile
-  const int total = sc.count * nk;              // stages of this workgroup
-  if (total == 0) return;
+  // Items: the tiles, or with splits > 1 (INT32 partial sums only) one per
+  // (K part, tile); part p's sums go to out + p * M * ldo.
+  const Sched sc = make_sched(blockIdx.x, gridDim.x, tiles_m, tiles_n, tiles_m * tiles_n * splits);
+  const int nk = K / kBK;                       // stages of the whole K
+  if (sc.count == 0) return;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -120,18 +132,20 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   // K offset, both in an SGPR. Otherwise rows past N or M are clamped to the
   // last valid row (their sums duplicate it and are stored over it with
   // identical values).
-  int ld_k = 0, ld_kt = 0, ld_rvn = 0, ld_rvm = 0;
+  int ld_k = 0, ld_kt = 0, ld_nk = 0, ld_rvn = 0, ld_rvm = 0;
   const int vo_w = r_l * (int)ldw + cw, vo_a = r_l * (int)lda + ca;
   __amdgpu_buffer_rsrc_t ld_w, ld_a;
   auto load_tile = [&](int k) {
-    int m0, n0;
-    tile_mn<kFull>(sc, k, m0, n0, M, N);
-    const int rn = (N - n0) < kBN ? (N - n0) : kBN;
-    const int rm = (M - m0) < kBM ? (M - m0) : kBM;
+    const Item it = item_of<kFull>(sc, k, M, N, nk, splits);
+    const int rn = (N - it.n0) < kBN ? (N - it.n0) : kBN;
+    const int rm = (M - it.m0) < kBM ? (M - it.m0) : kBM;
     ld_rvn = rn - 1;
     ld_rvm = rm - 1;
-    ld_w = buffer_rsrc(w + (int64_t)n0 * ldw, (uint32_t)(rn * ldw));
-    ld_a = buffer_rsrc(a + (int64_t)m0 * lda, (uint32_t)(rm * lda));
+    ld_nk = it.kbn;
+    // the buffers start at the item's first K byte
+    const int kb = it.kb0 * kBK;
+    ld_w = buffer_rsrc(w + (int64_t)it.n0 * ldw + kb, (uint32_t)(rn * ldw - kb));
+    ld_a = buffer_rsrc(a + (int64_t)it.m0 * lda + kb, (uint32_t)(rm * lda - kb));
   };
   load_tile(0);
   auto issue_next = [&](int slot) {
@@ -167,7 +181,7 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   // which it sinks the next stage's fragment reads, away from the MFMAs they
   // should hide behind.
   auto advance_loader = [&]() {
-    if (++ld_kt == nk) {
+    if (++ld_kt == ld_nk) {
       ld_kt = 0;
       if (++ld_k < sc.count) load_tile(ld_k);   // past the end: reloads of the last tile
     }
@@ -179,8 +193,8 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   // overwrite was last read by tile k - 2's epilogue, which every wave
   // finished before a barrier of tile k - 1.
   auto issue_scales = [&](int k) {
-    int m0, n0;
-    tile_mn<kFull>(sc, k, m0, n0, M, N);
+    const Item it = item_of<kFull>(sc, k, M, N, nk, splits);
+    const int m0 = it.m0, n0 = it.n0;
     int8_t* buf = scale_bufs + (k % kScaleBufs) * kBufBytes;
     // a buffer over the whole scale vector; indices past the end are clamped
     // to its last element (clamped rows reuse row M-1's scale). The lane
@@ -243,14 +257,14 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   auto epilogue = [&](int k) {
     const int el = lane_id();
     const int ir = el & 15, kq = el >> 4;
-    int m0, n0;
-    tile_mn<kFull>(sc, k, m0, n0, M, N);
+    const Item it = item_of<kFull>(sc, k, M, N, nk, splits);
+    const int m0 = it.m0, n0 = it.n0;
     const int n_wave = n0 + wn * 128;
     if (n_wave >= N) return;
     const int n_lane = n_wave + 8 * kq;
     const int m_lane = m0 + wm * (16 * kTM) + ir;
     if constexpr (kEpi == Epilogue::kInt32) {
-      int32_t* o = reinterpret_cast<int32_t*>(out);
+      int32_t* o = reinterpret_cast<int32_t*>(out) + (int64_t)it.part * M * ldo;
 #pragma unroll
       for (int j = 0; j < kTM; ++j) {
         int m = m_lane + 16 * j;
@@ -356,7 +370,8 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
       issue_scales(k + 1);
       pending_stores += kScaleLoads;
     }
-    for (int kt = 0; kt < nk; ++kt, ++s) {
+    const int kbn = item_of<kFull>(sc, k, M, N, nk, splits).kbn;
+    for (int kt = 0; kt < kbn; ++kt, ++s) {
       const int slot = s & 1;
       advance_loader();                    // to stage s+2
       // K step 0 (f0), K step 1's fragments read between its MFMAs
@@ -421,10 +436,12 @@ int device_cu_count() {
 hipError_t launch_gemm_pipelined(Epilogue epi, const int8_t* a, int64_t lda, const int8_t* w,
                                  int64_t ldw, const float* a_scale, const float* w_scale,
                                  const uint16_t* bias, void* out, int64_t ldo, int64_t M,
-                                 int64_t N, int64_t K, hipStream_t st) {
+                                 int64_t N, int64_t K, hipStream_t st, int splits) {
+  if (splits < 1 || (splits > 1 && epi != Epilogue::kInt32) || splits > (int)(K / pipe::kBK))
+    return hipErrorInvalidValue;
   const int tiles_m = (int)((M + pipe::kBM - 1) / pipe::kBM);
   const int tiles_n = (int)((N + pipe::kBN - 1) / pipe::kBN);
-  const int64_t tiles = (int64_t)tiles_m * tiles_n;
+  const int64_t tiles = (int64_t)tiles_m * tiles_n * splits;
   const int cus = device_cu_count();
   const int grid = (int)(tiles < cus ? tiles : cus);
   const dim3 block(pipe::kThreads);
@@ -433,7 +450,7 @@ hipError_t launch_gemm_pipelined(Epilogue epi, const int8_t* a, int64_t lda, con
 #define W8A8_PIPE_LAUNCH(E, F)                                                           \
   hipLaunchKernelGGL((pipe::gemm_i8_pipelined<E, F>), dim3(grid), block, 0, st, a, lda, w, \
                      ldw, a_scale, w_scale, bias, out, ldo, (int)M, (int)N, (int)K, tiles_m,  \
-                     tiles_n)
+                     tiles_n, splits)
 #define W8A8_PIPE_LAUNCH2(E)           \
   if (full) W8A8_PIPE_LAUNCH(E, true); \
   else W8A8_PIPE_LAUNCH(E, false)

@@ -33,11 +33,28 @@ enum class Epilogue { kPostscaleBf16, kInt32, kBlockwiseBf16, kPostscaleBiasBf16
 // launch at most one workgroup per CU.
 int device_cu_count();
 
-// Persistent pipelined kernel (post-scale and INT32 epilogues).
+// Persistent pipelined kernel (post-scale and INT32 epilogues). With
+// splits > 1 (INT32 only, splits <= K / 128) K is cut into `splits` parts of
+// whole 128-byte stages and part p's sums go to out + p * M * ldo.
 hipError_t launch_gemm_pipelined(Epilogue epi, const int8_t* a, int64_t lda, const int8_t* w,
                                  int64_t ldw, const float* a_scale, const float* w_scale,
                                  const uint16_t* bias, void* out, int64_t ldo, int64_t M,
-                                 int64_t N, int64_t K, hipStream_t st);
+                                 int64_t N, int64_t K, hipStream_t st, int splits = 1);
+
+// out[m, n] = bf16(fl32(fl32(fl32(sum_p part_p[m, n]) * a_scale[m]) * w_scale[n])
+// (+ bias[n])): the post-scale epilogue over INT32 partial sums
+// part_p = ws + p * M * N (each [M, N], row stride N).
+hipError_t launch_splitk_postscale(const int32_t* ws, int splits, int64_t M, int64_t N,
+                                   const float* a_scale, const float* w_scale,
+                                   const uint16_t* bias, uint16_t* out, int64_t ldo,
+                                   hipStream_t st);
+
+// K parts for a post-scale GEMM of this shape on `cus` compute units, from a
+// cost model of the split (fewer stages per work item against the partial
+// sums' HBM traffic and a fixed cost); 1 unless splitting saves a quarter of
+// the time. The W8A8_SPLIT_K environment variable overrides it (1 disables
+// splitting).
+int splitk_parts(int64_t M, int64_t N, int64_t K, int cus);
 
 // Persistent pipelined kernel with per-K-block scales.
 hipError_t launch_gemm_blockwise(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,

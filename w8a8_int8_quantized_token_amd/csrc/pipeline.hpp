@@ -37,18 +37,20 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// A workgroup's tiles: logical ids start + k * stride, k < count. Workgroup b
-// runs on XCD b % 8; each XCD owns a contiguous range of logical tiles, so
-// the rows its tiles share stay in that XCD's L2.
+// A workgroup's work items: logical ids start + k * stride, k < count. Workgroup
+// b runs on XCD b % 8; each XCD owns a contiguous range of logical ids, so
+// the rows its tiles share stay in that XCD's L2. Items default to the tiles;
+// a split-K GEMM has one item per (K part, tile), the part changing slowest.
 struct Sched {
   int start, stride, count, tiles_m, tiles_n;
 };
 
-__device__ __forceinline__ Sched make_sched(int b, int grid, int tiles_m, int tiles_n) {
+__device__ __forceinline__ Sched make_sched(int b, int grid, int tiles_m, int tiles_n,
+                                            int items = -1) {
   Sched s;
   s.tiles_m = tiles_m;
   s.tiles_n = tiles_n;
-  const int T = tiles_m * tiles_n;
+  const int T = items < 0 ? tiles_m * tiles_n : items;
   const int x = b % kXcds, j = b / kXcds;
   const int nwg = grid / kXcds + (x < grid % kXcds ? 1 : 0);     // workgroups on XCD x
   const int tx = T / kXcds + (x < T % kXcds ? 1 : 0);            // tiles of XCD x
@@ -60,9 +62,10 @@ __device__ __forceinline__ Sched make_sched(int b, int grid, int tiles_m, int ti
 }
 
 // M-grouped order: groups of kGroupM tile rows, n fastest within a group.
+// tile_of maps a tile id t < tiles_m * tiles_n; tile_mn a workgroup's k-th
+// item when the items are the tiles.
 template <int kBM, int kBN, int kGroupM>
-__device__ __forceinline__ void tile_mn(const Sched& s, int k, int& m0, int& n0) {
-  const int t = s.start + k * s.stride;
+__device__ __forceinline__ void tile_of(const Sched& s, int t, int& m0, int& n0) {
   const int span = kGroupM * s.tiles_n;
   const int g = t / span;
   const int first = g * kGroupM;
@@ -70,6 +73,11 @@ __device__ __forceinline__ void tile_mn(const Sched& s, int k, int& m0, int& n0)
   const int in = t - g * span;
   m0 = (first + in % gs) * kBM;
   n0 = (in / gs) * kBN;
+}
+
+template <int kBM, int kBN, int kGroupM>
+__device__ __forceinline__ void tile_mn(const Sched& s, int k, int& m0, int& n0) {
+  tile_of<kBM, kBN, kGroupM>(s, s.start + k * s.stride, m0, n0);
 }
 
 // Raw buffer resource over [base, base + bytes): the address of a load is an
