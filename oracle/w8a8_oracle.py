@@ -47,6 +47,13 @@ R12 bias of an Int8Linear (next row f2: "Reused Components", W8A8 Linear
     bullet, Int8Linear replaces Linear, which may carry a bias): added in fp32
     after both scales, before the one BF16 rounding:
     out = bf16(fl32(fl32(fl32(fl32(acc) * sa) * sw) + bias)).
+R13 the FFN activation between the up and down projections (next row f3;
+    "Differences From TurboDiffusion", W8A8-kernel row: the kernel is tuned
+    for the LTX FFN shapes; the pages do not name the activation): GELU in
+    its erf form, GELU(y) = y * Phi(y) = y/2 * erfc(-y/sqrt(2)), applied to
+    the BF16 output y of the up projection (post-scale and optional bias as
+    R5/R12), evaluated in fp64 and rounded once to BF16. The down
+    projection's per-token quantisation (R1-R3) then reads that BF16 tensor.
 
 Floating-point values are BF16 bit patterns (uint16) at the interface.
 """
@@ -59,6 +66,7 @@ __all__ = [
     "quantize_rows", "rmsnorm_inv_rms", "rmsnorm_bf16", "rmsnorm_quant",
     "layernorm_stats", "layernorm_bf16", "modulate_bf16", "layernorm_quant",
     "gemm_i32", "postscale_bf16", "postscale_bias_bf16", "fma_f32", "gemm_blockwise_bf16",
+    "f64_to_bf16", "gelu_f64", "gelu_bf16", "postscale_gelu_bf16",
     "w8a8_linear", "check_gemm_shape", "ShapeError", "bf16_ulp_distance",
 ]
 
@@ -95,6 +103,24 @@ def f32_to_bf16(x: np.ndarray) -> np.ndarray:
         rounded = np.where(nan, ((u >> np.uint64(16)) | np.uint64(0x40)).astype(np.uint16),
                            rounded)
     return rounded
+
+
+def f64_to_bf16(x: np.ndarray) -> np.ndarray:
+    """float64 -> BF16 bit patterns, one rounding (nearest, ties to even).
+
+    Goes through fp32 with round-to-odd: the value is cut toward zero to
+    fp32 and, if that was inexact, the last fp32 bit is set. fp32 keeps 16
+    more bits than BF16, so the final round-to-nearest-even to BF16 equals a
+    direct rounding of the fp64 value (no double-rounding error).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    f = x.astype(np.float32)
+    over = np.abs(f.astype(np.float64)) > np.abs(x)           # rounded away from zero
+    f = np.where(over, np.nextafter(f, np.float32(0)), f).astype(np.float32)
+    u = f.view(np.uint32).copy()
+    inexact = f.astype(np.float64) != x
+    u = np.where(inexact & ~np.isnan(x), u | np.uint32(1), u).astype(np.uint32)
+    return f32_to_bf16(u.view(np.float32))
 
 
 def bf16_ulp_distance(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
@@ -350,6 +376,29 @@ def postscale_bias_bf16(acc: np.ndarray, sa: np.ndarray, sw: np.ndarray,
     v = (t * np.asarray(sw, dtype=np.float32)[None, :]).astype(np.float32)
     v = (v + bf16_to_f32(bias_bits)[None, :]).astype(np.float32)
     return f32_to_bf16(v)
+
+
+def gelu_f64(y_bits: np.ndarray) -> np.ndarray:
+    """GELU(y) = y * Phi(y) = y/2 * erfc(-y / sqrt(2)) in fp64 on BF16 values y
+    (R13). erfc rather than 1 + erf, which loses all its digits for large
+    negative y."""
+    from scipy.special import erfc
+    y = bf16_to_f32(y_bits).astype(np.float64)
+    return 0.5 * y * erfc(-y / np.sqrt(2.0))
+
+
+def gelu_bf16(y_bits: np.ndarray) -> np.ndarray:
+    """h = bf16(GELU(y)) (R13): the fp64 value rounded once to BF16."""
+    return f64_to_bf16(gelu_f64(y_bits))
+
+
+def postscale_gelu_bf16(acc: np.ndarray, sa: np.ndarray, sw: np.ndarray,
+                        bias_bits: np.ndarray | None = None) -> np.ndarray:
+    """The up projection with its activation (R13): GELU of the BF16 post-scale
+    output (R5, or R12 with a bias)."""
+    if bias_bits is None:
+        return gelu_bf16(postscale_bf16(acc, sa, sw))
+    return gelu_bf16(postscale_bias_bf16(acc, sa, sw, bias_bits))
 
 
 # ---------------------------------------------------------------------------
