@@ -194,6 +194,30 @@ w8a8_status_t w8a8_gemm_postscale_bias(const int8_t* a, int64_t lda, const int8_
                                        int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
+ * w8a8_gemm_postscale_gelu -- w8a8_gemm_postscale (optionally with a bias)
+ * followed by the FFN activation, GELU in its erf form, on the BF16 output:
+ * the up projection of a feed-forward block in one kernel.
+ *
+ * Passage: "Differences From TurboDiffusion", W8A8-kernel row (the kernel
+ * serves the LTX FFN shapes) with the epilogue of w8a8_gemm_postscale. The
+ * pages do not name the activation; GELU (erf form) is the reading taken.
+ *
+ *   y[m,n]   = bf16(fl32(fl32(fl32(acc) * a_scale[m]) * w_scale[n]) (+ bias[n]))
+ *   out[m,n] = bf16(y/2 * erfc(-y / sqrt(2)))   (computed in fp32 from y)
+ *
+ *   bias  [N] BF16, 16-byte aligned, or NULL for none (input)
+ * Everything else, requirements and errors as w8a8_gemm_postscale; the output
+ * must not overlap the bias either. The GELU is computed in fp32 with erfcf
+ * and rounded to BF16; for every finite BF16 y that equals the correctly
+ * rounded GELU (checked exhaustively). The per-token quantisation of out
+ * (w8a8_quant_rows) gives the down projection's input.
+ */
+w8a8_status_t w8a8_gemm_postscale_gelu(const int8_t* a, int64_t lda, const int8_t* w,
+                                       int64_t ldw, const float* a_scale, const float* w_scale,
+                                       const uint16_t* bias, uint16_t* out, int64_t ldo,
+                                       int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * w8a8_gemm_blockwise -- blockwise-scaled W8A8 GEMM (the original
  * TurboDiffusion scheme, "Differences From TurboDiffusion", W8A8 kernel row).
  *

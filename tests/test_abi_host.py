@@ -36,6 +36,7 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"w8a8_quant_rows", "w8a8_rmsnorm_quant", "w8a8_layernorm_quant",
                           "w8a8_gemm_postscale", "w8a8_gemm_postscale_bias",
+                          "w8a8_gemm_postscale_gelu",
                           "w8a8_gemm_blockwise", "w8a8_gemm_i32", "w8a8_status_string",
                           "w8a8_last_error", "w8a8_version"}
     raw = ctypes.CDLL(w8.LIB_PATH)
@@ -135,7 +136,7 @@ def test_layernorm_quant_optional_vectors_may_be_null():
 def gemm(fn="w8a8_gemm_postscale", a=P, lda=256, w=Q, ldw=256, sa=S, sw=S + 0x100000,
          out=O, ldo=128, M=64, N=128, K=256):
     f = getattr(w8.lib(), fn)
-    if fn == "w8a8_gemm_postscale_bias":
+    if fn in ("w8a8_gemm_postscale_bias", "w8a8_gemm_postscale_gelu"):
         return f(a, lda, w, ldw, sa, sw, S + 0x200000, out, ldo, M, N, K, None)
     if fn == "w8a8_gemm_i32":
         return f(a, lda, w, ldw, out, ldo, M, N, K, None)
@@ -164,7 +165,7 @@ GEMM_CASES = [
 
 @pytest.mark.parametrize("kwargs,status", GEMM_CASES)
 @pytest.mark.parametrize("fn", ["w8a8_gemm_postscale", "w8a8_gemm_postscale_bias",
-                                "w8a8_gemm_blockwise"])
+                                "w8a8_gemm_postscale_gelu", "w8a8_gemm_blockwise"])
 def test_gemm_rejects(fn, kwargs, status):
     assert gemm(fn, **kwargs) == status
 
@@ -192,6 +193,20 @@ def test_gemm_bias_rejects():
     assert bias_gemm(O + 0x1000) == INVALID                          # bias inside the output
     assert bias_gemm(O - 0x100, N=256) == INVALID                    # bias runs into the output
     assert bias_gemm(None, M=0) == OK                                # empty call: a no-op
+
+
+def gelu_gemm(bias, out=O, M=64, N=128):
+    return w8.lib().w8a8_gemm_postscale_gelu(P, 256, Q, 256, S, S + 0x100000, bias, out, N,
+                                             M, N, 256, None)
+
+
+def test_gemm_gelu_rejects():
+    assert gelu_gemm(S + 0x200008) == UNSUPPORTED                    # bias not 16-byte aligned
+    assert gelu_gemm(O + 0x1000) == INVALID                          # bias inside the output
+    assert gelu_gemm(None, out=S) == INVALID                         # output over a scale
+    assert gelu_gemm(None, M=0) == OK                                # empty call: a no-op
+    assert w8.lib().w8a8_gemm_postscale_gelu(P, 256, Q, 256, None, S, None, O, 128, 64, 128,
+                                             256, None) == INVALID   # null scale
 
 
 def test_empty_calls_are_noops():

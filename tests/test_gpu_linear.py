@@ -142,3 +142,21 @@ def test_replace_linear_with_int8():
         ulp_report(bf16_from_dev(h), ref, "replaced first layer")
         y = block(x)
     assert y.shape == (65, 100) and torch.isfinite(y.float()).all()
+
+
+def test_int8_linear_gelu_activation():
+    log("Int8Linear(activation='gelu') against the oracle, and its BF16 fallback")
+    M, K, N = 300, 512, 1280
+    x = W.random_bits((M, K), 171)
+    wb = W.random_bits((N, K), 172, std=0.05)
+    b = bias_bits(N, 173)
+    lin = w8.Int8Linear(bf16_to_dev(wb), bf16_to_dev(b), activation="gelu")
+    out = lin(bf16_to_dev(x))
+    torch.cuda.synchronize()
+    _, qa_o, sa_o, qw_o, sw_o, acc = O.w8a8_linear(x, wb, b)
+    ref = O.postscale_gelu_bf16(acc, sa_o, sw_o, b)
+    assert np.array_equal(bf16_from_dev(out), ref)
+    fb = w8.Int8Linear(bf16_to_dev(W.random_bits((100, 256), 174)), activation="gelu")
+    assert not fb.int8
+    xs = bf16_to_dev(W.random_bits((7, 256), 175))
+    assert torch.equal(fb(xs), torch.nn.functional.gelu(torch.nn.functional.linear(xs, fb.weight)))

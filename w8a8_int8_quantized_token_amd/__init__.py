@@ -58,6 +58,7 @@ _SIGS = {
                              _p, _p, _p],
     "w8a8_gemm_postscale": [_p, _i64, _p, _i64, _p, _p, _p, _i64, _i64, _i64, _i64, _p],
     "w8a8_gemm_postscale_bias": [_p, _i64, _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p],
+    "w8a8_gemm_postscale_gelu": [_p, _i64, _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p],
     "w8a8_gemm_blockwise": [_p, _i64, _p, _i64, _p, _p, _p, _i64, _i64, _i64, _i64, _p],
     "w8a8_gemm_i32": [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p],
 }
@@ -222,11 +223,20 @@ def _gemm_args(a, w, out, out_dtype):
 
 def w8a8_gemm_postscale(a: torch.Tensor, w: torch.Tensor, a_scale: torch.Tensor,
                         w_scale: torch.Tensor, out: torch.Tensor | None = None, stream=None,
-                        bias: torch.Tensor | None = None):
+                        bias: torch.Tensor | None = None, gelu: bool = False):
     """out[M,N] (BF16) = bf16(acc * a_scale[m] * w_scale[n] (+ bias[n])), acc the
     exact INT32 sum over K of a[m,k] * w[n,k]; with a bias this calls
-    w8a8_gemm_postscale_bias."""
+    w8a8_gemm_postscale_bias; with gelu=True, w8a8_gemm_postscale_gelu (GELU,
+    erf form, of that BF16 output)."""
     M, N, K, out = _gemm_args(a, w, out, torch.bfloat16)
+    if gelu:
+        if bias is not None:
+            _vec(bias, torch.bfloat16, N, "bias")
+        st = _lib.w8a8_gemm_postscale_gelu(_ptr(a), _ld(a), _ptr(w), _ld(w), _ptr(a_scale),
+                                           _ptr(w_scale), None if bias is None else _ptr(bias),
+                                           _ptr(out), _ld(out), M, N, K, _stream(stream))
+        _check(st, "w8a8_gemm_postscale_gelu")
+        return out
     if bias is None:
         st = _lib.w8a8_gemm_postscale(_ptr(a), _ld(a), _ptr(w), _ld(w), _ptr(a_scale),
                                       _ptr(w_scale), _ptr(out), _ld(out), M, N, K, _stream(stream))

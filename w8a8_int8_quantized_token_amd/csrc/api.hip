@@ -235,6 +235,27 @@ w8a8_status_t w8a8_gemm_postscale_bias(const int8_t* a, int64_t lda, const int8_
                   "w8a8_gemm_postscale_bias launch");
 }
 
+w8a8_status_t w8a8_gemm_postscale_gelu(const int8_t* a, int64_t lda, const int8_t* w,
+                                       int64_t ldw, const float* a_scale, const float* w_scale,
+                                       const uint16_t* bias, uint16_t* out, int64_t ldo,
+                                       int64_t M, int64_t N, int64_t K, void* stream) {
+  w8a8_status_t st = check_gemm_common(a, lda, w, ldw, out, ldo, 2, M, N, K);
+  if (st != W8A8_OK) return st;
+  if (M == 0) return ok();
+  if (!a_scale || !w_scale) return fail(W8A8_ERR_INVALID_ARGUMENT, "null scale pointer");
+  if (!aligned(a_scale, 4) || !aligned(w_scale, 4)) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "scales must be 4-byte aligned");
+  if (bias && !aligned(bias, 16)) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "bias must be 16-byte aligned");
+  const size_t ob = span_bytes(M, N, ldo, 2);
+  if (overlap(out, ob, a_scale, (size_t)M * 4) || overlap(out, ob, w_scale, (size_t)N * 4) ||
+      (bias && overlap(out, ob, bias, (size_t)N * 2)))
+    return fail(W8A8_ERR_INVALID_ARGUMENT, "output overlaps a scale or the bias");
+  return from_hip(w8a8::launch_gemm(bias ? w8a8::Epilogue::kPostscaleBiasGeluBf16
+                                         : w8a8::Epilogue::kPostscaleGeluBf16,
+                                    a, lda, w, ldw, a_scale, w_scale, bias, out, ldo, M, N, K,
+                                    (hipStream_t)stream),
+                  "w8a8_gemm_postscale_gelu launch");
+}
+
 w8a8_status_t w8a8_gemm_blockwise(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
                                   const float* a_scale, const float* w_scale, uint16_t* out,
                                   int64_t ldo, int64_t M, int64_t N, int64_t K, void* stream) {

@@ -33,6 +33,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, b);
 }
 
+// fp32 -> the fp32 value of its BF16 rounding (nearest even).
+__device__ __forceinline__ float round_bf16(float v) { return bf16_lo(pack_bf16x2(v, 0.0f)); }
+
+// GELU, erf form, of a BF16 value y: y/2 * erfc(-y / sqrt(2)) in fp32. erfc
+// instead of 1 + erf keeps the digits of the small negative outputs.
+__device__ __forceinline__ float gelu_erf(float y) {
+  return 0.5f * y * erfcf(-y * 0.70710678118654752f);
+}
+
 // ---------------------------------------------------------------------------
 // Wave reductions (64 lanes)
 // ---------------------------------------------------------------------------

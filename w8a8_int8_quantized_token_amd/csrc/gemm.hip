@@ -16,7 +16,9 @@ hipError_t launch_gemm(Epilogue epi, const int8_t* a, int64_t lda, const int8_t*
   if (M == 0) return hipSuccess;
   switch (epi) {
     case Epilogue::kPostscaleBf16:
-    case Epilogue::kPostscaleBiasBf16: {
+    case Epilogue::kPostscaleBiasBf16:
+    case Epilogue::kPostscaleGeluBf16:
+    case Epilogue::kPostscaleBiasGeluBf16: {
       // Too few tiles to fill the chip: K in parts, INT32 partial sums in a
       // stream-ordered workspace, then one pass that adds them and applies
       // the epilogue (bit-identical to the single pass). If the workspace
@@ -30,7 +32,7 @@ hipError_t launch_gemm(Epilogue epi, const int8_t* a, int64_t lda, const int8_t*
           if (e == hipSuccess)
             e = launch_splitk_postscale(
                 static_cast<const int32_t*>(ws), parts, M, N, a_scale, w_scale,
-                epi == Epilogue::kPostscaleBiasBf16 ? bias : nullptr,
+                epilogue_has_bias(epi) ? bias : nullptr, epilogue_has_gelu(epi),
                 reinterpret_cast<uint16_t*>(out), ldo, st);
           const hipError_t f = hipFreeAsync(ws, st);
           return e != hipSuccess ? e : f;

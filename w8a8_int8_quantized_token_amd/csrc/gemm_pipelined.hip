@@ -59,6 +59,45 @@ constexpr int kBiasBytes = kWaves * 256;       // one dword wave-load per wave (
 constexpr int kScaleBufs = 3;                  // tile k's scales sit in buffer k % 3
 constexpr int kGroupM = 8;
 
+// GELU of a BF16 value y (to BF16), by ranges of its exponent field e:
+//  * e <= 121 (|y| < 2^-5): y/2 * (1 + y * sqrt(2/pi)) in fp32 rounds to the
+//    same BF16 as the exact GELU (the next series term is below half a BF16
+//    unit there; checked for every such y);
+//  * y >= 4 (e >= 129, positive): GELU(y) rounds to y (from 2.78125 on);
+//  * y <= -16 (e >= 131, negative): GELU(y) rounds to -0 (from -13.5625 on);
+//  * else: a 2048-entry table (4 KiB of LDS) built at kernel start with the
+//    erfc formula, which is correctly rounded for every BF16 input: positive
+//    y with e in [122, 128] at (bits & 0x7FFF) - (122 << 7), negative y with
+//    e in [122, 130] 896 entries further.
+constexpr int kGeluFirstExp = 122;
+constexpr int kGeluPos = 7 * 128, kGeluNeg = 9 * 128;
+constexpr int kGeluTable = kGeluPos + kGeluNeg;   // entries (uint16)
+static_assert(kGeluTable == 2048, "two 4-byte table halves per thread-pair");
+
+__device__ __forceinline__ uint16_t gelu_table_entry(int i) {
+  const uint32_t neg = i >= kGeluPos ? 1u : 0u;
+  const uint32_t mag = (uint32_t)(kGeluFirstExp << 7) + (uint32_t)(neg ? i - kGeluPos : i);
+  const float y = __uint_as_float(((neg << 15) | mag) << 16);
+  return (uint16_t)(pack_bf16x2(gelu_erf(y), 0.0f) & 0xFFFFu);
+}
+
+// One BF16 GELU (bits in, bits out) given the table entry t read for it.
+__device__ __forceinline__ uint32_t gelu_select(uint32_t bits, uint32_t t) {
+  const uint32_t a = bits & 0x7FFFu, e = a >> 7, neg = bits >> 15;
+  const float y = __uint_as_float(bits << 16);
+  const float poly = (0.5f * y) * (1.0f + 0.7978845608028654f * y);
+  const uint32_t small = pack_bf16x2(poly, 0.0f) & 0xFFFFu;
+  const uint32_t far = neg ? 0x8000u : bits;          // -0 far left, y far right
+  const uint32_t far_e = neg ? 131u : 129u;
+  return e <= (uint32_t)(kGeluFirstExp - 1) ? small : (e >= far_e ? far : t);
+}
+__device__ __forceinline__ uint32_t gelu_index(uint32_t bits) {
+  const int a = (int)(bits & 0x7FFFu) - (kGeluFirstExp << 7);
+  const bool neg = (bits >> 15) != 0;
+  const int hi = neg ? kGeluNeg - 1 : kGeluPos - 1;
+  return (uint32_t)((a < 0 ? 0 : (a > hi ? hi : a)) + (neg ? kGeluPos : 0));
+}
+
 // 128-byte LDS rows hold 8 chunks of 16 bytes; logical chunk c of row r sits
 // at c ^ key(r). Weight rows are read in the permuted slot order (row slot
 // 4 q + e of tile i is row 32 (i / 2) + 8 q + 4 (i % 2) + e), activation rows
@@ -104,18 +143,28 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
                        void* __restrict__ out, int64_t ldo, int M, int N, int K, int tiles_m,
                        int tiles_n, int splits) {
   constexpr bool kScales = kEpi != Epilogue::kInt32;
-  constexpr bool kBias = kEpi == Epilogue::kPostscaleBiasBf16;
+  constexpr bool kBias = epilogue_has_bias(kEpi);
+  constexpr bool kGelu = epilogue_has_gelu(kEpi);
   // a tile's scales, then (with a bias) its biases
   constexpr int kBufBytes = kScaleBytes + (kBias ? kBiasBytes : 0);
   constexpr int kScaleLoads = kBias ? 2 : 1;   // wave-loads per wave per tile
-  __shared__ __attribute__((aligned(1024))) int8_t lds[kSlots * kSlotBytes + kScaleBufs * kBufBytes];
+  constexpr int kGeluBytes = kGelu ? kGeluTable * 2 : 0;
+  __shared__ __attribute__((aligned(1024)))
+  int8_t lds[kSlots * kSlotBytes + kScaleBufs * kBufBytes + kGeluBytes];
   int8_t* const scale_bufs = lds + kSlots * kSlotBytes;
+  int8_t* const gelu_lds = scale_bufs + kScaleBufs * kBufBytes;
 
   // Items: the tiles, or with splits > 1 (INT32 partial sums only) one per
   // (K part, tile); part p's sums go to out + p * M * ldo.
   const Sched sc = make_sched(blockIdx.x, gridDim.x, tiles_m, tiles_n, tiles_m * tiles_n * splits);
   const int nk = K / kBK;                       // stages of the whole K
   if (sc.count == 0) return;
+  if constexpr (kGelu) {
+    // the GELU table; the prologue's barrier publishes it
+    uint16_t* tab = reinterpret_cast<uint16_t*>(gelu_lds);
+    for (int i = threadIdx.x; i < kGeluTable; i += kThreads) tab[i] = gelu_table_entry(i);
+    wait_lgkmcnt0();
+  }
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -330,13 +379,30 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
                 v[2 * q + 1] = v[2 * q + 1] + bf16_hi(bw[4 * pp + q]);
               }
             }
+            v4u packed{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                       pack_bf16x2(v[6], v[7])};
+            if constexpr (kGelu) {   // the FFN activation on the BF16 Linear output
+              const uint32_t tab = lds_addr(gelu_lds);
+              uint32_t t[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const uint32_t bits = (packed[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                asm volatile("ds_read_u16 %0, %1" : "=v"(t[e]) : "v"(tab + 2 * gelu_index(bits)));
+              }
+              asm volatile("s_waitcnt lgkmcnt(0)"
+                           : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]),
+                             "+v"(t[5]), "+v"(t[6]), "+v"(t[7])
+                           :
+                           : "memory");
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                packed[q] = gelu_select(packed[q] & 0xFFFFu, t[2 * q]) |
+                            (gelu_select(packed[q] >> 16, t[2 * q + 1]) << 16);
+            }
             // Non-temporal: the output streams past the caches instead of
             // evicting the activation and weight rows the next tiles read.
             uint16_t* dst = o + (int64_t)m * ldo + n_lane + 32 * p;
-            __builtin_nontemporal_store(
-                v4u{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                    pack_bf16x2(v[6], v[7])},
-                reinterpret_cast<v4u*>(dst));
+            __builtin_nontemporal_store(packed, reinterpret_cast<v4u*>(dst));
           }
         }
       }
@@ -454,9 +520,16 @@ hipError_t launch_gemm_pipelined(Epilogue epi, const int8_t* a, int64_t lda, con
 #define W8A8_PIPE_LAUNCH2(E)           \
   if (full) W8A8_PIPE_LAUNCH(E, true); \
   else W8A8_PIPE_LAUNCH(E, false)
-  if (epi == Epilogue::kInt32) { W8A8_PIPE_LAUNCH2(Epilogue::kInt32); }
-  else if (epi == Epilogue::kPostscaleBiasBf16) { W8A8_PIPE_LAUNCH2(Epilogue::kPostscaleBiasBf16); }
-  else { W8A8_PIPE_LAUNCH2(Epilogue::kPostscaleBf16); }
+  switch (epi) {
+    case Epilogue::kInt32: W8A8_PIPE_LAUNCH2(Epilogue::kInt32); break;
+    case Epilogue::kPostscaleBf16: W8A8_PIPE_LAUNCH2(Epilogue::kPostscaleBf16); break;
+    case Epilogue::kPostscaleBiasBf16: W8A8_PIPE_LAUNCH2(Epilogue::kPostscaleBiasBf16); break;
+    case Epilogue::kPostscaleGeluBf16: W8A8_PIPE_LAUNCH2(Epilogue::kPostscaleGeluBf16); break;
+    case Epilogue::kPostscaleBiasGeluBf16:
+      W8A8_PIPE_LAUNCH2(Epilogue::kPostscaleBiasGeluBf16);
+      break;
+    default: return hipErrorInvalidValue;
+  }
 #undef W8A8_PIPE_LAUNCH2
 #undef W8A8_PIPE_LAUNCH
   return hipGetLastError();

@@ -27,7 +27,20 @@ hipError_t launch_layernorm_quant(const uint16_t* x, const uint16_t* gamma, cons
                                   int64_t rows, int64_t cols, int64_t ldx, int8_t* q, int64_t ldq,
                                   float* scale, float* mean, float* rstd, hipStream_t st);
 
-enum class Epilogue { kPostscaleBf16, kInt32, kBlockwiseBf16, kPostscaleBiasBf16 };
+enum class Epilogue {
+  kPostscaleBf16,
+  kInt32,
+  kBlockwiseBf16,
+  kPostscaleBiasBf16,
+  kPostscaleGeluBf16,       // GELU of the BF16 post-scale output
+  kPostscaleBiasGeluBf16,   // GELU of the BF16 post-scale-plus-bias output
+};
+constexpr bool epilogue_has_bias(Epilogue e) {
+  return e == Epilogue::kPostscaleBiasBf16 || e == Epilogue::kPostscaleBiasGeluBf16;
+}
+constexpr bool epilogue_has_gelu(Epilogue e) {
+  return e == Epilogue::kPostscaleGeluBf16 || e == Epilogue::kPostscaleBiasGeluBf16;
+}
 
 // Compute units of the current device (cached per device); persistent grids
 // launch at most one workgroup per CU.
@@ -42,11 +55,12 @@ hipError_t launch_gemm_pipelined(Epilogue epi, const int8_t* a, int64_t lda, con
                                  int64_t N, int64_t K, hipStream_t st, int splits = 1);
 
 // out[m, n] = bf16(fl32(fl32(fl32(sum_p part_p[m, n]) * a_scale[m]) * w_scale[n])
-// (+ bias[n])): the post-scale epilogue over INT32 partial sums
-// part_p = ws + p * M * N (each [M, N], row stride N).
+// (+ bias[n])), then with gelu its GELU rounded to BF16: the post-scale
+// epilogue over INT32 partial sums part_p = ws + p * M * N (each [M, N], row
+// stride N).
 hipError_t launch_splitk_postscale(const int32_t* ws, int splits, int64_t M, int64_t N,
                                    const float* a_scale, const float* w_scale,
-                                   const uint16_t* bias, uint16_t* out, int64_t ldo,
+                                   const uint16_t* bias, bool gelu, uint16_t* out, int64_t ldo,
                                    hipStream_t st);
 
 // K parts for a post-scale GEMM of this shape on `cus` compute units, from a

@@ -5,8 +5,8 @@
 // of K, scales applied in the epilogue. Integer addition is exact and
 // associative, so K may be cut into parts whose INT32 partial sums (from the
 // pipelined kernel's INT32 epilogue) add up to exactly the full sum; this
-// kernel adds them and applies the same fp32 epilogue, in the same order, as
-// the single-pass kernel, so the output is bit-identical to it.
+// kernel adds them and applies the same fp32 epilogue (and GELU), in the same
+// order, as the single-pass kernel, so the output is bit-identical to it.
 //
 // One thread per 8 consecutive outputs of a row: per part two 16-byte loads,
 // one 16-byte store. The partial sums are read once (non-temporal).
@@ -20,7 +20,7 @@ namespace splitk {
 
 constexpr int kThreads = 256;
 
-template <bool kBias>
+template <bool kBias, bool kGelu>
 __global__ __launch_bounds__(kThreads)
 void postscale_kernel(const int32_t* __restrict__ ws, int splits, int M, int N,
                       const float* __restrict__ a_scale, const float* __restrict__ w_scale,
@@ -54,6 +54,10 @@ void postscale_kernel(const int32_t* __restrict__ ws, int splits, int M, int N,
         v[2 * q + 1] = v[2 * q + 1] + bf16_hi(b[q]);
       }
     }
+    if constexpr (kGelu) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = gelu_erf(round_bf16(v[e]));
+    }
     __builtin_nontemporal_store(v4u{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                                     pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])},
                                 reinterpret_cast<v4u*>(out + (int64_t)m * ldo + n));
@@ -64,7 +68,7 @@ void postscale_kernel(const int32_t* __restrict__ ws, int splits, int M, int N,
 
 hipError_t launch_splitk_postscale(const int32_t* ws, int splits, int64_t M, int64_t N,
                                    const float* a_scale, const float* w_scale,
-                                   const uint16_t* bias, uint16_t* out, int64_t ldo,
+                                   const uint16_t* bias, bool gelu, uint16_t* out, int64_t ldo,
                                    hipStream_t st) {
   if (splits < 1 || N % 8 != 0) return hipErrorInvalidValue;
   const int64_t units = M * (N / 8);
@@ -72,12 +76,14 @@ hipError_t launch_splitk_postscale(const int32_t* ws, int splits, int64_t M, int
   const int64_t want = (units + splitk::kThreads - 1) / splitk::kThreads;
   const int64_t cap = (int64_t)device_cu_count() * 8;
   const int grid = (int)(want < cap ? want : cap);
-  if (bias)
-    hipLaunchKernelGGL(splitk::postscale_kernel<true>, dim3(grid), dim3(splitk::kThreads), 0, st,
-                       ws, splits, (int)M, (int)N, a_scale, w_scale, bias, out, ldo);
-  else
-    hipLaunchKernelGGL(splitk::postscale_kernel<false>, dim3(grid), dim3(splitk::kThreads), 0,
-                       st, ws, splits, (int)M, (int)N, a_scale, w_scale, bias, out, ldo);
+#define W8A8_SPLITK_LAUNCH(B, G)                                                           \
+  hipLaunchKernelGGL((splitk::postscale_kernel<B, G>), dim3(grid), dim3(splitk::kThreads), 0, \
+                     st, ws, splits, (int)M, (int)N, a_scale, w_scale, bias, out, ldo)
+  if (bias && gelu) W8A8_SPLITK_LAUNCH(true, true);
+  else if (bias) W8A8_SPLITK_LAUNCH(true, false);
+  else if (gelu) W8A8_SPLITK_LAUNCH(false, true);
+  else W8A8_SPLITK_LAUNCH(false, false);
+#undef W8A8_SPLITK_LAUNCH
   return hipGetLastError();
 }
 

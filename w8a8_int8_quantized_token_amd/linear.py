@@ -29,10 +29,16 @@ def int8_shape_supported(out_features: int, in_features: int) -> bool:
 
 class Int8Linear(torch.nn.Module):
     """y = x W^T (+ b) with W quantised per output channel at construction and
-    x quantised per token on every call (BF16 in, BF16 out)."""
+    x quantised per token on every call (BF16 in, BF16 out). With
+    activation="gelu" the layer is an FFN up projection: y = GELU(x W^T (+ b))
+    (erf form) on the BF16 Linear output, fused into the GEMM's epilogue."""
 
-    def __init__(self, weight: torch.Tensor, bias: torch.Tensor | None = None):
+    def __init__(self, weight: torch.Tensor, bias: torch.Tensor | None = None,
+                 activation: str | None = None):
         super().__init__()
+        if activation not in (None, "gelu"):
+            raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, f"unknown activation {activation!r}")
+        self.activation = activation
         if not isinstance(weight, torch.Tensor) or weight.device.type != "cuda":
             raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, "Int8Linear needs a weight on a GPU")
         weight = weight.detach().to(torch.bfloat16).contiguous()
@@ -52,12 +58,12 @@ class Int8Linear(torch.nn.Module):
         self.register_buffer("weight_scale", sw)
 
     @classmethod
-    def from_linear(cls, linear: torch.nn.Linear) -> "Int8Linear":
-        return cls(linear.weight, linear.bias)
+    def from_linear(cls, linear: torch.nn.Linear, activation: str | None = None) -> "Int8Linear":
+        return cls(linear.weight, linear.bias, activation)
 
     def extra_repr(self) -> str:
         return (f"in_features={self.in_features}, out_features={self.out_features}, "
-                f"bias={self.bias is not None}, int8={self.int8}")
+                f"bias={self.bias is not None}, activation={self.activation}, int8={self.int8}")
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         if x.device.type != "cuda":
@@ -71,11 +77,12 @@ class Int8Linear(torch.nn.Module):
             try:
                 qa, sa = w8a8_quant_rows(x2)
                 out = w8a8_gemm_postscale(qa, self.qweight, sa, self.weight_scale,
-                                          bias=self.bias)
+                                          bias=self.bias, gelu=self.activation == "gelu")
                 return out.reshape(*x.shape[:-1], self.out_features)
             except W8A8Unsupported:
                 pass
-        return torch.nn.functional.linear(x, self.weight, self.bias)
+        y = torch.nn.functional.linear(x, self.weight, self.bias)
+        return torch.nn.functional.gelu(y) if self.activation == "gelu" else y
 
 
 def replace_linear_with_int8(module: torch.nn.Module, select=None) -> int:
