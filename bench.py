@@ -36,7 +36,7 @@ METRIC = "W8A8 GEMM INT8 TOPS + % INT8 MFMA peak at DiT FFN shapes; quant GB/s"
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, TOP/s
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 N_ROTATE = 3                   # activation buffers cycled so inputs come from HBM
-GEMM_SOURCES = ("gemm.hip", "gemm_pipelined.hip", "gemm_blockwise.hip", "pipeline.hpp",
+GEMM_SOURCES = ("gemm.hip", "gemm_pipelined.hip", "gemm_blockwise.hip", "splitk.hip", "pipeline.hpp",
                 "device_common.hpp", "launch.hpp")
 
 
