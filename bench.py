@@ -136,6 +136,7 @@ def main():
     gamma = up(W.gamma_bits(wl)) if wl.norm else None
     mod_scale = up(W.mod_bits(wl, "mod_scale")) if wl.layernorm else None
     mod_shift = up(W.mod_bits(wl, "mod_shift")) if wl.layernorm else None
+    bias = up(W.bias_bits(wl)) if wl.bias_std > 0 else None
     xs = [up(x_host)]
     for _ in range(N_ROTATE - 1):
         xs.append(xs[0].clone())
@@ -191,9 +192,13 @@ def main():
         def gemm():
             w8.w8a8_gemm_blockwise(qa, qw, sa, sw, out=out)
     else:
-        gemm_name = "gemm_postscale"
+        # the epilogue's extras (bias, GELU) and, where the library splits K
+        # (few tokens), its two passes all count as the GEMM
+        gemm_name = ("gemm_postscale" + ("_bias" if bias is not None else "")
+                     + ("_gelu" if wl.gelu else "")
+                     + ("_splitk" if w8.splitk_parts(M, N, K) > 1 else ""))
         def gemm():
-            w8.w8a8_gemm_postscale(qa, qw, sa, sw, out=out)
+            w8.w8a8_gemm_postscale(qa, qw, sa, sw, out=out, bias=bias, gelu=wl.gelu)
 
     ops = 2 * M * N * K
     for i in range(args.warmup):
@@ -239,14 +244,17 @@ def main():
     # ---- the pages' yardstick: torch's BF16 Linear on the same shape ---------
     if not args.no_bf16:
         wt = w_bf16
+        def bf16_linear(x):
+            y = torch.nn.functional.linear(x, wt, bias)
+            return torch.nn.functional.gelu(y) if wl.gelu else y
         for i in range(3):
-            torch.nn.functional.linear(xs[i % N_ROTATE], wt)
+            bf16_linear(xs[i % N_ROTATE])
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         reps = 10
         e0.record(stream)
         for i in range(reps):
-            torch.nn.functional.linear(xs[i % N_ROTATE], wt)
+            bf16_linear(xs[i % N_ROTATE])
         e1.record(stream)
         torch.cuda.synchronize()
         bf16_ms = e0.elapsed_time(e1) / reps
@@ -300,8 +308,16 @@ def cpu_baseline(wl, x_host, w_host, budget_s):
     chunk = 256
     t_path = 0.0
     g = None
+    import workloads as W
+    b = W.bias_bits(wl) if wl.bias_std > 0 else None
+
+    def epilogue(acc, sa):
+        if wl.gelu:
+            return O.postscale_gelu_bf16(acc, sa, sw, b)
+        if b is not None:
+            return O.postscale_bias_bf16(acc, sa, sw, b)
+        return O.postscale_bf16(acc, sa, sw)
     if wl.norm or wl.layernorm:
-        import workloads as W
         g = W.gamma_bits(wl) if wl.norm else None
         msc = W.mod_bits(wl, "mod_scale") if wl.layernorm else None
         msh = W.mod_bits(wl, "mod_shift") if wl.layernorm else None
@@ -311,16 +327,16 @@ def cpu_baseline(wl, x_host, w_host, budget_s):
         t1 = time.perf_counter()
         if wl.norm:
             qa, sa, _ = O.rmsnorm_quant(x, g, wl.eps)
-            O.postscale_bf16(O.gemm_i32(qa, qw), sa, sw)
+            epilogue(O.gemm_i32(qa, qw), sa)
         elif wl.layernorm:
             qa, sa, _, _ = O.layernorm_quant(x, wl.eps, scale_bits=msc, shift_bits=msh)
-            O.postscale_bf16(O.gemm_i32(qa, qw), sa, sw)
+            epilogue(O.gemm_i32(qa, qw), sa)
         elif wl.blockwise:
             qa, sa = O.quantize_groups(x, 1, 128)
             O.gemm_blockwise_bf16(qa, sa, qw, sw)
         else:
             qa, sa = O.quantize_rows(x)
-            O.postscale_bf16(O.gemm_i32(qa, qw), sa, sw)
+            epilogue(O.gemm_i32(qa, qw), sa)
         t_path += time.perf_counter() - t1
         rows_done = r1
         chunk = min(chunk * 2, 4096)

@@ -253,6 +253,17 @@ const char* w8a8_last_error(void);
 /* Library version string. */
 const char* w8a8_version(void);
 
+/*
+ * w8a8_gemm_splitk_parts -- how many K parts the post-scale entry points
+ * (w8a8_gemm_postscale, _bias, _gelu) use for an M x N x K GEMM on the current
+ * device: 1 for a single pass, else the parts of the split-K path (exact INT32
+ * partial sums in a stream-ordered workspace of parts * M * N * 4 bytes, then
+ * one epilogue pass). Host only, launches nothing. Passage: "Differences From
+ * TurboDiffusion", paragraph under the table (one INT32 accumulation over K;
+ * integer sums may be formed in parts and added exactly).
+ */
+int32_t w8a8_gemm_splitk_parts(int64_t M, int64_t N, int64_t K);
+
 #ifdef __cplusplus
 }
 #endif

@@ -42,6 +42,8 @@ WORKLOAD_SHAPES = {
     "blockwise_small": "M=1000 N=K=5120 (1x128 quant -> blockwise GEMM)",
     "blockwise_large": "M=32760 N=K=5120 (1x128 quant -> blockwise GEMM)",
     "ln_up_proj": "M=28672 N=16384 K=4096 (LayerNorm+modulation+quant -> post-scale GEMM)",
+    "up_proj_gelu": "M=28672 N=16384 K=4096 (RMSNorm+quant -> post-scale GEMM + bias + GELU)",
+    "small_m": "M=256 N=5120 K=13824 (quant -> split-K: INT32 partial sums + post-scale pass)",
     "tiny": "M=64 N=128 K=256",
 }
 
@@ -52,7 +54,10 @@ def short_name(kernel: str) -> str:
     if "gemm_i8_" in kernel:
         m = re.search(r"Epilogue\)(\d)|EpilogueE(\d)", kernel)
         e = (m.group(1) or m.group(2)) if m else "?"
-        return {"0": "gemm_postscale", "1": "gemm_i32"}.get(e, "gemm")
+        return {"0": "gemm_postscale", "1": "gemm_i32", "3": "gemm_postscale_bias",
+                "4": "gemm_postscale_gelu", "5": "gemm_postscale_bias_gelu"}.get(e, "gemm")
+    if "splitk" in kernel and "postscale_kernel" in kernel:
+        return "splitk_postscale"
     if "rmsnorm_quant_kernel" in kernel:
         return "rmsnorm_quant"
     if "layernorm_quant_kernel" in kernel:

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
                           "w8a8_gemm_postscale", "w8a8_gemm_postscale_bias",
                           "w8a8_gemm_postscale_gelu",
                           "w8a8_gemm_blockwise", "w8a8_gemm_i32", "w8a8_status_string",
-                          "w8a8_last_error", "w8a8_version"}
+                          "w8a8_last_error", "w8a8_version", "w8a8_gemm_splitk_parts"}
     raw = ctypes.CDLL(w8.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -246,3 +246,14 @@ def test_int8_linear_rejects_cpu_weights():
     assert not w8.linear.int8_shape_supported(100, 256)
     assert not w8.linear.int8_shape_supported(128, 200)
     assert not w8.linear.int8_shape_supported(128, w8.W8A8_MAX_K + 128)
+
+
+def test_splitk_parts_query():
+    # no GPU here: the model runs with its 256-unit default
+    assert w8.splitk_parts(28672, 16384, 4096) == 1          # tiles fill the chip
+    assert w8.splitk_parts(1000, 5120, 5120) == 1            # partial sums would cost more
+    assert w8.splitk_parts(129, 5120, 13824) > 1
+    assert w8.splitk_parts(0, 128, 256) == 1 and w8.splitk_parts(4, 128, 0) == 1
+    for M, N, K in ((1, 256, 2048), (256, 5120, 13824), (33, 128, 8192)):
+        p = w8.splitk_parts(M, N, K)
+        assert 1 <= p <= K // 128 and p * M * N * 4 <= 1 << 30

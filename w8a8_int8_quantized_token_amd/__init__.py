@@ -72,8 +72,11 @@ _lib.w8a8_last_error.argtypes = []
 _lib.w8a8_last_error.restype = ctypes.c_char_p
 _lib.w8a8_version.argtypes = []
 _lib.w8a8_version.restype = ctypes.c_char_p
+_lib.w8a8_gemm_splitk_parts.argtypes = [_i64, _i64, _i64]
+_lib.w8a8_gemm_splitk_parts.restype = ctypes.c_int32
 
-EXPORTED_SYMBOLS = tuple(_SIGS) + ("w8a8_status_string", "w8a8_last_error", "w8a8_version")
+EXPORTED_SYMBOLS = tuple(_SIGS) + ("w8a8_status_string", "w8a8_last_error", "w8a8_version",
+                                   "w8a8_gemm_splitk_parts")
 
 
 def lib() -> ctypes.CDLL:
@@ -83,6 +86,11 @@ def lib() -> ctypes.CDLL:
 
 def w8a8_version() -> str:
     return _lib.w8a8_version().decode()
+
+
+def splitk_parts(M: int, N: int, K: int) -> int:
+    """K parts the post-scale GEMMs use for this shape on the current device."""
+    return int(_lib.w8a8_gemm_splitk_parts(M, N, K))
 
 
 def _check(status: int, name: str) -> None:

@@ -111,6 +111,11 @@ const char* w8a8_last_error(void) { return g_last_error.c_str(); }
 
 const char* w8a8_version(void) { return "w8a8-gfx950 0.1"; }
 
+int32_t w8a8_gemm_splitk_parts(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K < 128) return 1;
+  return w8a8::splitk_parts(M, N, K, w8a8::device_cu_count());
+}
+
 w8a8_status_t w8a8_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                               int64_t group_rows, int64_t group_cols, int8_t* q, int64_t ldq,
                               float* scale, void* stream) {

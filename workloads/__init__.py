@@ -25,6 +25,10 @@ The shapes and value distributions are those of the five workloads:
 * ``ln_up_proj`` the up_proj shapes with a LayerNorm prologue instead of the
                 RMSNorm: no affine, eps 1e-6, adaLN modulation scale and shift
                 [4096] ~N(0,0.2); X ~N(0,1); W ~N(0,0.02)
+* ``up_proj_gelu`` the up_proj shapes as an FFN up projection: bias [16384]
+                ~N(0,0.1), GELU on the output
+* ``small_m``   X [256,13824] = BF16(GELU_erf(z)) (a short sequence against
+                the down projection's weight); W [5120,13824] ~N(0,0.01)
 """
 from __future__ import annotations
 
@@ -34,7 +38,7 @@ import torch
 
 CHUNK_ROWS = 1024
 
-_TAGS = {"x": 1, "w": 2, "gamma": 3, "outlier": 4, "mod_scale": 5, "mod_shift": 6}
+_TAGS = {"x": 1, "w": 2, "gamma": 3, "outlier": 4, "mod_scale": 5, "mod_shift": 6, "bias": 7}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -56,6 +60,8 @@ class Workload:
     blockwise: bool = False     # 1x128 activation / 128x128 weight scales
     layernorm: bool = False     # LayerNorm + adaLN modulation prologue (no affine)
     mod_std: float = 0.2
+    bias_std: float = 0.0       # > 0: a Linear bias [N] ~N(0, bias_std)
+    gelu: bool = False          # GELU (erf form) on the Linear output
 
     @property
     def gemm_ops(self) -> int:
@@ -75,6 +81,9 @@ WORKLOADS = {
                                 1.0, 0.02, blockwise=True),
     "ln_up_proj": Workload("ln_up_proj", 28672, 16384, 4096, 1007, "normal", 1.0, 0.02,
                            layernorm=True),
+    "up_proj_gelu": Workload("up_proj_gelu", 28672, 16384, 4096, 1008, "normal", 1.0, 0.02,
+                             norm=True, bias_std=0.1, gelu=True),
+    "small_m": Workload("small_m", 256, 5120, 13824, 1009, "gelu", 1.0, 0.01),
 }
 
 
@@ -143,6 +152,12 @@ def mod_bits(wl: Workload, which: str) -> np.ndarray:
     """adaLN modulation vector [K] ("mod_scale" or "mod_shift") ~ N(0, mod_std) as BF16 bits."""
     z = torch.randn(wl.K, generator=_gen(wl.seed, which, 0), dtype=torch.float32)
     return _to_bf16_bits(z * wl.mod_std)
+
+
+def bias_bits(wl: Workload) -> np.ndarray:
+    """Linear bias [N] ~ N(0, bias_std) as BF16 bits."""
+    z = torch.randn(wl.N, generator=_gen(wl.seed, "bias", 0), dtype=torch.float32)
+    return _to_bf16_bits(z * wl.bias_std)
 
 
 def random_bits(shape, seed: int, std: float = 1.0, mean: float = 0.0) -> np.ndarray:
