@@ -16,7 +16,9 @@
  *
  * Conventions shared by every entry point:
  *   - Every data pointer is a DEVICE pointer, owned by the caller. The library
- *     allocates nothing, keeps no state between calls and never synchronises.
+ *     keeps no state between calls and never synchronises. It allocates
+ *     nothing, except the split-K workspace of the post-scale GEMMs (see
+ *     w8a8_gemm_postscale), which is stream-ordered on the caller's stream.
  *   - Row-major layouts; leading dimensions (ld*) are in ELEMENTS.
  *   - BF16 values travel as their 16-bit patterns (uint16_t).
  *   - `stream` is a hipStream_t passed as an opaque pointer (NULL = the
@@ -169,6 +171,16 @@ w8a8_status_t w8a8_layernorm_quant(const uint16_t* x, const uint16_t* gamma,
  * Requirements (else W8A8_ERR_UNSUPPORTED_SHAPE): K % 128 == 0, 128 <= K <=
  * W8A8_MAX_K, N % 128 == 0; a, w, out 16-byte aligned; lda % 16 == 0,
  * ldw % 16 == 0, ldo % 8 == 0; scales 4-byte aligned. M >= 0 arbitrary.
+ *
+ * Split-K: when the 256 x 256 output tiles would leave most compute units
+ * idle (few tokens, long K) the call cuts K into parts
+ * (w8a8_gemm_splitk_parts), writes their exact INT32 partial sums to a
+ * workspace taken with hipMallocAsync on `stream` (parts * M * N * 4 bytes,
+ * at most 1 GiB) and released with hipFreeAsync on it after one more pass
+ * adds them and applies this epilogue. The output is bit-identical to the
+ * single pass. If the workspace cannot be had the single pass runs. The
+ * environment variable W8A8_SPLIT_K=1 disables splitting (=n forces n parts).
+ * The same holds for w8a8_gemm_postscale_bias and w8a8_gemm_postscale_gelu.
  */
 w8a8_status_t w8a8_gemm_postscale(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
                                   const float* a_scale, const float* w_scale,
