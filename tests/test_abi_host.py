@@ -257,3 +257,25 @@ def test_splitk_parts_query():
     for M, N, K in ((1, 256, 2048), (256, 5120, 13824), (33, 128, 8192)):
         p = w8.splitk_parts(M, N, K)
         assert 1 <= p <= K // 128 and p * M * N * 4 <= 1 << 30
+
+
+@pytest.mark.parametrize("env", ["1", "5", "0"])
+def test_splitk_env_override(env):
+    # W8A8_SPLIT_K is read once per process, so each setting runs in a child
+    # (host only: the query launches nothing).  An override is still capped by
+    # the number of 128-byte K stages and by the 1 GiB workspace limit.
+    import subprocess
+    import sys
+    shapes = [(129, 5120, 13824), (2048, 4096, 4096), (129, 5120, 256), (28672, 16384, 4096)]
+    code = ("import w8a8_int8_quantized_token_amd as w8; "
+            f"print(*[w8.splitk_parts(*s) for s in {shapes!r}])")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       env={**os.environ, "W8A8_SPLIT_K": env}, timeout=120)
+    assert r.returncode == 0, r.stderr
+    small, mid, short_k, huge = map(int, r.stdout.split())
+    assert huge == 1                       # one part alone is 1.9 GB of INT32 partial sums
+    if env == "0":                         # not an override: the cost model decides
+        assert small > 1 and mid == 1 and short_k == 1
+    else:
+        f = int(env)
+        assert small == f and mid == f and short_k == min(f, 256 // 128)
