@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calib", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
+    p.add_argument("--ceiling", action="store_true",
+                   help="only time the post-scale GEMM's main loop alone (probe library) on "
+                        "constant and on random operands")
     p.add_argument("--summarize", metavar="PROF_DIR",
                    help="summarise rocprofv3 results under PROF_DIR into profiles/ (no GPU)")
     return p.parse_args()
@@ -78,6 +81,74 @@ def copy_calibration(steps: int) -> None:
     ms = e0.elapsed_time(e1) / steps
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copy_ms": round(ms, 4),
                       "copy_gbs": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
+def mainloop_ceiling() -> None:
+    """The post-scale GEMM's inner loop alone (libw8a8_probe.so: the same LDS
+    ring, fragment reads and MFMA stream, no epilogue, operands L2-resident),
+    timed on constant operands, on uniformly random ones, and on random ones
+    without the stage refills. The first is the rate the schedule allows; the
+    drop to the second is what the power drawn by random operands costs."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "w8a8_int8_quantized_token_amd", "libw8a8_probe.so")
+    if not os.path.exists(path):
+        sys.exit("libw8a8_probe.so is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    lib.w8a8_probe_mainloop_workgroups.restype = ctypes.c_int
+    lib.w8a8_probe_mainloop.restype = ctypes.c_int
+    lib.w8a8_probe_mainloop.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                                        ctypes.c_void_p]
+    torch.cuda.init()
+    grid = lib.w8a8_probe_mainloop_workgroups()
+    if grid < 1:
+        sys.exit("cannot read the compute-unit count")
+    src = torch.empty(2 << 20, dtype=torch.int8, device="cuda")
+    sink = torch.empty(grid * 512, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    stages = 2048
+    ops = 2.0 * 256 * 256 * 128 * grid * stages
+    rand = torch.randint(-127, 128, (src.numel(),), dtype=torch.int8,
+                         generator=torch.Generator().manual_seed(1234))
+    results = {}
+    for name, data, refill in (("constant", None, 1), ("random", rand, 1),
+                               ("random_no_refill", rand, 0)):
+        if data is None:
+            src.fill_(1)
+        else:
+            src.copy_(data)
+
+        def call():
+            rc = lib.w8a8_probe_mainloop(src.data_ptr(), src.numel(), stages, refill,
+                                         sink.data_ptr(), sink.numel(), stream.cuda_stream)
+            if rc != 0:
+                sys.exit(f"w8a8_probe_mainloop failed ({rc})")
+
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        call()
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        # >= 200 ms of load first: the engine clock ramps over ~150 ms
+        for _ in range(max(3, int(200.0 / max(e0.elapsed_time(e1), 0.01)))):
+            call()
+        reps = 20
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        results[name] = {"us_per_launch": round(ms * 1e3, 1),
+                         "us_per_stage": round(ms * 1e3 / stages, 4),
+                         "tops": round(ops / (ms * 1e-3) / 1e12, 1),
+                         "frac_of_int8_peak": round(ops / (ms * 1e-3) / 5.0e15, 4)}
+        print(f"{name:18s} {results[name]}", flush=True)
+    print(json.dumps({"probe": "gemm_mainloop", "workgroups": grid, "stages": stages,
+                      "block_tile": [256, 256, 128], "peak_tops": 5000.0,
+                      "results": results}), flush=True)
 
 
 def source_hash(*names) -> str:
@@ -111,6 +182,9 @@ def main():
         return
     if args.copy_calib:
         copy_calibration(args.steps)
+        return
+    if args.ceiling:
+        mainloop_ceiling()
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the W8A8 Linear is "

@@ -279,3 +279,19 @@ def test_splitk_env_override(env):
     else:
         f = int(env)
         assert small == f and mid == f and short_k == min(f, 256 // 128)
+
+
+def test_probe_library_loads_and_rejects_bad_arguments():
+    # the main-loop ceiling probe is a library of its own (not part of the C ABI);
+    # bad arguments are refused before anything touches a device
+    import ctypes
+    path = os.path.join(ROOT, "w8a8_int8_quantized_token_amd", "libw8a8_probe.so")
+    lib = ctypes.CDLL(path)
+    f = lib.w8a8_probe_mainloop
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_int64, ctypes.c_void_p]
+    assert f(None, 2 << 20, 8, 1, None, 1 << 20, None) == 1          # null buffers
+    assert f(1 << 20, (2 << 20) - 1, 8, 1, 1 << 20, 1 << 20, None) == 1   # buffer too small
+    assert f(1 << 20, 2 << 20, 0, 1, 1 << 20, 1 << 20, None) == 1    # no stages
+    assert f(1 << 20, 2 << 20, 8, 2, 1 << 20, 1 << 20, None) == 1    # refill not 0/1

@@ -3,10 +3,12 @@
     python -m w8a8_int8_quantized_token_amd.build
 
 Compiles every .hip source under csrc/ with hipcc for gfx950 only and links
-one shared library next to this file. The flags fix the floating-point
-contract the kernels rely on: no fast-math, no implicit FMA contraction,
-IEEE fp32 division / square root, denormals kept, and no packed-fp32 VALU
-instructions.
+one shared library next to this file. The measurement probe under probe/
+(the GEMM's main loop alone, for its throughput ceiling) is linked into a
+library of its own, libw8a8_probe.so, which only bench.py --ceiling loads.
+The flags fix the floating-point contract the kernels rely on: no
+fast-math, no implicit FMA contraction, IEEE fp32 division / square root,
+denormals kept, and no packed-fp32 VALU instructions.
 """
 from __future__ import annotations
 
@@ -19,6 +21,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw8a8.so")
+PROBE_DIR = os.path.join(HERE, "probe")
+PROBE_LIB = os.path.join(HERE, "libw8a8_probe.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -47,20 +51,28 @@ def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *sources(), "-o", tmp]
+def _link(srcs: list[str], includes: list[str], out: str, verbose: bool) -> str:
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS]
+    for inc in includes:
+        cmd += ["-I", inc]
+    cmd += [*srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libw8a8.so")
+        raise RuntimeError("hipcc failed building " + os.path.basename(out))
     if verbose and res.stderr.strip():
         sys.stderr.write(res.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    _link(sorted(os.path.join(PROBE_DIR, f) for f in os.listdir(PROBE_DIR) if f.endswith(".hip")),
+          [], PROBE_LIB, verbose)
+    return _link(sources(), [os.path.join(ROOT, "include"), CSRC], LIB, verbose)
 
 
 if __name__ == "__main__":
