@@ -35,6 +35,10 @@ void postscale_kernel(const int32_t* __restrict__ ws, int splits, int M, int N,
     const int32_t* src = ws + (int64_t)m * N + n;
     v4i s0 = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src));
     v4i s1 = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src + 4));
+    // unrolled so that several parts' loads are in flight at once: with few
+    // outputs the grid is small and each part's loads would otherwise wait
+    // out a full memory round trip
+#pragma unroll 8
     for (int p = 1; p < splits; ++p) {
       s0 += __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src + p * slice));
       s1 += __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src + p * slice + 4));
@@ -100,25 +104,42 @@ int splitk_parts(int64_t M, int64_t N, int64_t K, int cus) {
     while (parts > 1 && parts * bytes_per_part > kMaxWorkspace) --parts;
     return (int)parts;
   }
-  // Cost model in microseconds, from measurements on MI355X: a 128-byte K
-  // stage of a 256 x 256 tile takes about 1.3; the partial sums cost their
-  // write and read at about 4 TB/s; the extra pass and the workspace cost
-  // about 15 in all. Split only where it saves a quarter of the time.
+  // Cost model in microseconds, fitted to timings of split and single passes
+  // on MI355X (M from 64 to 2048, N from 1024 to 16384, K from 4096 to 13824,
+  // 1 to 24 parts):
+  //  * single pass: 1.3 per 128-byte K stage of a 256 x 256 tile, per round
+  //    of tiles over the compute units;
+  //  * split: per round of work items, 1.3 per stage plus 3 for the item's
+  //    prologue and INT32 epilogue; 11 for the extra pass and the workspace;
+  //    0.286 per MB of partial sums (written once, read once); and never
+  //    below 25, what the host needs to issue the allocation, two launches
+  //    and the release.
+  // Split only if that saves 15%, and then take the fewest parts within 5%
+  // of the best (fewer partial bytes, same predicted time).
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  const double stage_us = 1.3, bytes_per_us = 4.0e6, fixed_us = 15.0;
+  const double stage_us = 1.3, item_us = 3.0, fixed_us = 11.0, us_per_byte = 0.286e-6,
+               floor_us = 25.0;
   const double single = (double)((tiles + cus - 1) / cus) * nk * stage_us;
-  int best = 1;
-  double best_us = 0.75 * single;
+  double est[65] = {0};
+  double best_us = 0.0;
+  int64_t last = 1;
   for (int64_t parts = 2; parts <= nk && parts <= 64; ++parts) {
     if (parts * bytes_per_part > kMaxWorkspace) break;
     const double rounds = (double)((tiles * parts + cus - 1) / cus);
-    const double us = rounds * (double)((nk + parts - 1) / parts) * stage_us +
-                      (2.0 * parts + 0.5) * (double)bytes_per_part / bytes_per_us + fixed_us;
-    if (us < best_us) {
-      best_us = us;
-      best = (int)parts;
-    }
+    double us = rounds * ((double)((nk + parts - 1) / parts) * stage_us + item_us) + fixed_us +
+                us_per_byte * (double)(parts * bytes_per_part);
+    us = us > floor_us ? us : floor_us;
+    est[parts] = us;
+    if (last == 1 || us < best_us) best_us = us;
+    last = parts;
   }
+  if (last == 1 || best_us >= 0.85 * single) return 1;
+  int best = 1;
+  for (int64_t parts = 2; parts <= last; ++parts)
+    if (est[parts] <= 1.05 * best_us) {
+      best = (int)parts;
+      break;
+    }
   return best;
 }
 
