@@ -219,10 +219,12 @@ w8a8_status_t w8a8_gemm_postscale_bias(const int8_t* a, int64_t lda, const int8_
  *
  *   bias  [N] BF16, 16-byte aligned, or NULL for none (input)
  * Everything else, requirements and errors as w8a8_gemm_postscale; the output
- * must not overlap the bias either. The GELU is computed in fp32 with erfcf
- * and rounded to BF16; for every finite BF16 y that equals the correctly
- * rounded GELU (checked exhaustively). The per-token quantisation of out
- * (w8a8_quant_rows) gives the down projection's input.
+ * must not overlap the bias either. For every finite BF16 y the result is
+ * the correctly rounded GELU (checked exhaustively); +inf gives +inf, -inf
+ * and NaN give NaN. The kernel reads most results from a table built with
+ * erfcf in fp32 and takes bf16(y/2) where |y| < 2^-9 (exact there). The
+ * per-token quantisation of out (w8a8_quant_rows) gives the down
+ * projection's input.
  */
 w8a8_status_t w8a8_gemm_postscale_gelu(const int8_t* a, int64_t lda, const int8_t* w,
                                        int64_t ldw, const float* a_scale, const float* w_scale,

@@ -29,12 +29,14 @@ def exact_report(got, ref, what):
 
 def test_gelu_every_bf16_value():
     """acc = 1 everywhere and w_scale = 1, so row m's output is GELU of the
-    BF16 value a_scale[m]: one row per BF16 bit pattern."""
+    BF16 value a_scale[m]: one row per BF16 bit pattern, the non-finite ones
+    included (y/2 * erfc(-y / sqrt(2)) gives +inf for +inf and NaN for -inf
+    and NaN)."""
     log("GELU epilogue over all 65536 BF16 patterns")
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     vals = O.bf16_to_f32(bits)
     finite = np.isfinite(vals)
-    sa = np.where(finite, vals, 0.0).astype(np.float32)
+    sa = vals.astype(np.float32)
     M, N, K = 65536, 128, 128
     qa = np.zeros((M, K), np.int8)
     qa[:, 0] = 1
@@ -46,6 +48,11 @@ def test_gelu_every_bf16_value():
     got = bf16_from_dev(out)
     assert np.all(got == got[:, :1])                       # every column the same
     exact_report(got[finite, 0], O.gelu_bf16(bits[finite]), "GELU of every finite BF16 value")
+    g = O.bf16_to_f32(got[:, 0])
+    assert g[0x7F80] == np.inf                             # +inf
+    assert np.isnan(g[0xFF80])                             # -inf
+    nan_in = np.isnan(vals)
+    assert nan_in.sum() == 254 and np.all(np.isnan(g[nan_in]))
 
 
 SHAPES = [((64, 128, 256), 151), ((1000, 384, 512), 152), ((257, 640, 1024), 153),

@@ -60,42 +60,47 @@ constexpr int kScaleBufs = 3;                  // tile k's scales sit in buffer 
 constexpr int kGroupM = 8;
 
 // GELU of a BF16 value y (to BF16), by ranges of its exponent field e:
-//  * e <= 121 (|y| < 2^-5): y/2 * (1 + y * sqrt(2/pi)) in fp32 rounds to the
-//    same BF16 as the exact GELU (the next series term is below half a BF16
-//    unit there; checked for every such y);
-//  * y >= 4 (e >= 129, positive): GELU(y) rounds to y (from 2.78125 on);
-//  * y <= -16 (e >= 131, negative): GELU(y) rounds to -0 (from -13.5625 on);
-//  * else: a 2048-entry table (4 KiB of LDS) built at kernel start with the
-//    erfc formula, which is correctly rounded for every BF16 input: positive
-//    y with e in [122, 128] at (bits & 0x7FFF) - (122 << 7), negative y with
-//    e in [122, 130] 896 entries further.
-constexpr int kGeluFirstExp = 122;
-constexpr int kGeluPos = 7 * 128, kGeluNeg = 9 * 128;
-constexpr int kGeluTable = kGeluPos + kGeluNeg;   // entries (uint16)
-static_assert(kGeluTable == 2048, "two 4-byte table halves per thread-pair");
+//  * e <= 117 (|y| < 2^-9): GELU(y) rounds to the BF16 rounding of y/2
+//    (GELU(y) / (y/2) - 1 is about y * sqrt(2/pi), below half a BF16 unit
+//    there; checked for every such y), and y * 0.5f is exact in fp32;
+//  * e in [118, 130], either sign: a 3328-entry table (6.5 KiB of LDS) built
+//    at kernel start with the erfc formula, which is correctly rounded for
+//    every BF16 input there: entry (bits & 0x7FFF) - (118 << 7), plus 1664
+//    for negative y;
+//  * e >= 131 (|y| >= 16): y for positive y (GELU(y) rounds to y from
+//    2.78125 on), -0 for negative y (from -13.5625 on); +inf gives +inf,
+//    -inf and NaN give NaN, as y/2 * erfc(-y / sqrt(2)) does.
+// A table index is formed for every value (clamped into the table) and the
+// entry is read; the selection then picks the entry, y/2 or the far value.
+constexpr int kGeluFirstExp = 118;
+constexpr int kGeluHalf = 13 * 128;            // entries per sign: e = 118 .. 130
+constexpr int kGeluTable = 2 * kGeluHalf;      // entries (uint16)
+constexpr uint32_t kGeluLow = (uint32_t)kGeluFirstExp << 7;
 
 __device__ __forceinline__ uint16_t gelu_table_entry(int i) {
-  const uint32_t neg = i >= kGeluPos ? 1u : 0u;
-  const uint32_t mag = (uint32_t)(kGeluFirstExp << 7) + (uint32_t)(neg ? i - kGeluPos : i);
+  const uint32_t neg = i >= kGeluHalf ? 1u : 0u;
+  const uint32_t mag = kGeluLow + (uint32_t)(neg ? i - kGeluHalf : i);
   const float y = __uint_as_float(((neg << 15) | mag) << 16);
   return (uint16_t)(pack_bf16x2(gelu_erf(y), 0.0f) & 0xFFFFu);
 }
 
+// Table index of BF16 bits; values outside the table read its last entry of
+// their sign (and discard it).
+__device__ __forceinline__ uint32_t gelu_index(uint32_t bits) {
+  const uint32_t idx = (bits & 0x7FFFu) - kGeluLow;   // wraps below the table
+  const uint32_t c = idx < (uint32_t)(kGeluHalf - 1) ? idx : (uint32_t)(kGeluHalf - 1);
+  return c + (bits >> 15) * (uint32_t)kGeluHalf;
+}
+
 // One BF16 GELU (bits in, bits out) given the table entry t read for it.
 __device__ __forceinline__ uint32_t gelu_select(uint32_t bits, uint32_t t) {
-  const uint32_t a = bits & 0x7FFFu, e = a >> 7, neg = bits >> 15;
-  const float y = __uint_as_float(bits << 16);
-  const float poly = (0.5f * y) * (1.0f + 0.7978845608028654f * y);
-  const uint32_t small = pack_bf16x2(poly, 0.0f) & 0xFFFFu;
-  const uint32_t far = neg ? 0x8000u : bits;          // -0 far left, y far right
-  const uint32_t far_e = neg ? 131u : 129u;
-  return e <= (uint32_t)(kGeluFirstExp - 1) ? small : (e >= far_e ? far : t);
-}
-__device__ __forceinline__ uint32_t gelu_index(uint32_t bits) {
-  const int a = (int)(bits & 0x7FFFu) - (kGeluFirstExp << 7);
+  const uint32_t a = bits & 0x7FFFu;
+  const uint32_t idx = a - kGeluLow;
+  const uint32_t half = pack_bf16x2(__uint_as_float(bits << 16) * 0.5f, 0.0f) & 0xFFFFu;
   const bool neg = (bits >> 15) != 0;
-  const int hi = neg ? kGeluNeg - 1 : kGeluPos - 1;
-  return (uint32_t)((a < 0 ? 0 : (a > hi ? hi : a)) + (neg ? kGeluPos : 0));
+  // e >= 131: finite -> y or -0; +inf -> +inf; -inf -> NaN; NaN -> itself
+  const uint32_t far = a < 0x7F80u ? (neg ? 0x8000u : bits) : (bits == 0xFF80u ? 0xFFC0u : bits);
+  return idx < (uint32_t)kGeluHalf ? t : (a < kGeluLow ? half : far);
 }
 
 // 128-byte LDS rows hold 8 chunks of 16 bytes; logical chunk c of row r sits
