@@ -1,10 +1,11 @@
 """The up projection with its FFN activation (GELU, erf form) on the GPU,
 against the oracle (R13: GELU of the BF16 post-scale output, rounded once).
 
-The device evaluates GELU in fp32 (erfcf) and rounds to BF16. Over every
-finite BF16 input that equals the correctly rounded value (the first test,
-which covers GELU's whole input domain), so every GELU output below is
-required bit for bit; then the rest of the feed-forward chain (per-token
+The device evaluates GELU from fp32 erfcf (a table of it in the fused
+epilogue, erfcf itself in the split-K pass) and rounds to BF16. Over every
+finite BF16 input that equals the correctly rounded value (the first two
+tests, which cover GELU's whole input domain on both paths), so every GELU
+output below is required bit for bit; then the rest of the feed-forward chain (per-token
 quantisation of the GELU output, the down projection) is checked exactly.
 """
 from __future__ import annotations
@@ -53,6 +54,48 @@ def test_gelu_every_bf16_value():
     assert np.isnan(g[0xFF80])                             # -inf
     nan_in = np.isnan(vals)
     assert nan_in.sum() == 254 and np.all(np.isnan(g[nan_in]))
+
+
+_SPLIT_CHILD = r"""
+import sys
+import numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+import oracle as O
+import w8a8_int8_quantized_token_amd as w8
+bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+vals = O.bf16_to_f32(bits)
+finite = np.isfinite(vals)
+M, N, K = 65536, 128, 256
+assert w8.splitk_parts(M, N, K) == 2
+qa = np.zeros((M, K), np.int8); qa[:, 0] = 1
+qw = np.zeros((N, K), np.int8); qw[:, 0] = 1
+dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+out = w8.w8a8_gemm_postscale(dev(qa), dev(qw), dev(vals.astype(np.float32)),
+                             dev(np.ones(N, np.float32)), gelu=True)
+torch.cuda.synchronize()
+got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+assert np.all(got == got[:, :1])
+bad = int(np.count_nonzero(got[finite, 0] != O.gelu_bf16(bits[finite])))
+g = O.bf16_to_f32(got[:, 0])
+ok = bad == 0 and g[0x7F80] == np.inf and np.isnan(g[0xFF80]) and np.all(np.isnan(g[np.isnan(vals)]))
+print("split-K GELU mismatches", bad, "special values ok" if ok else "special values WRONG", flush=True)
+sys.exit(0 if ok else 1)
+"""
+
+
+def test_gelu_every_bf16_value_split_k():
+    """The same over the split-K path, whose reduce pass computes GELU with
+    erfcf itself: forced to 2 parts (W8A8_SPLIT_K is read once per process,
+    so this runs in a child process)."""
+    import os
+    import subprocess
+    import sys
+    log("GELU in the split-K reduce pass over all 65536 BF16 patterns (child process)")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _SPLIT_CHILD, root], capture_output=True,
+                       text=True, timeout=240, env={**os.environ, "W8A8_SPLIT_K": "2"})
+    log("  " + (r.stdout.strip() or r.stderr.strip()[-400:]))
+    assert r.returncode == 0, r.stdout + r.stderr[-2000:]
 
 
 SHAPES = [((64, 128, 256), 151), ((1000, 384, 512), 152), ((257, 640, 1024), 153),
