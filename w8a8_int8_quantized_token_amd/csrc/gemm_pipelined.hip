@@ -24,12 +24,13 @@
 //    to back: the next tile's first stages are in flight during an epilogue.
 //    Workgroup b sits on XCD b % 8; each XCD owns a contiguous, M-grouped
 //    range of tiles so shared rows stay in that XCD's L2.
-//  * Weight rows are the MFMA "A" operand with permuted row slots: per
-//    16-byte store, the four lanes of a token hold 32 consecutive output
-//    channels, so one store instruction writes 16 tokens x 64 contiguous
-//    bytes (16-byte pieces scattered over twice as many lines cost the
-//    epilogue about 40% more time). The stores are non-temporal; with the
-//    scattered pieces that was slower, with whole 64-byte runs it is faster.
+//  * Weight rows are the MFMA "A" operand with permuted row slots: the four
+//    lanes of a token hold 32 consecutive output channels in each of two
+//    packed values (16-byte pieces scattered over more lines cost the
+//    epilogue about 40% more time), and a swap between lanes 8 apart pairs
+//    them so that one store instruction writes 8 tokens x 128 contiguous
+//    bytes, whole lines. The stores are non-temporal: with whole lines they
+//    write exactly the output's bytes (half lines cost a third more).
 //  * With M and N of at least one tile, the last tile row and column are
 //    moved back to end at M and N (they overlap their neighbours, whose
 //    rows they recompute and store again with identical values), so every
@@ -364,12 +365,7 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
         }
 #pragma unroll
         for (int j = 0; j < kTM; ++j) {
-          // Rows past M (clamped tiles only) hold exactly row M-1's sums
-          // (their loads were clamped to it) and its scale, so they store row
-          // M-1's values to row M-1: every lane issues its stores and the
-          // per-tile store count stays fixed.
-          int m = m_lane + 16 * j;
-          if constexpr (!kFull) m = m < M ? m : M - 1;
+          v4u pk[2];   // token m_lane + 16 j, channels 64 hf + 32 pp + 8 kq + [0, 8)
 #pragma unroll
           for (int pp = 0; pp < 2; ++pp) {
             const int p = 2 * hf + pp;
@@ -404,11 +400,37 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
                 packed[q] = gelu_select(packed[q] & 0xFFFFu, t[2 * q]) |
                             (gelu_select(packed[q] >> 16, t[2 * q + 1]) << 16);
             }
-            // Non-temporal: the output streams past the caches instead of
-            // evicting the activation and weight rows the next tiles read.
-            uint16_t* dst = o + (int64_t)m * ldo + n_lane + 32 * p;
-            __builtin_nontemporal_store(packed, reinterpret_cast<v4u*>(dst));
+            pk[pp] = packed;
           }
+          // Whole 128-byte lines per store: lanes ir and ir ^ 8 of each
+          // 16-lane row swap one value (DPP row rotate by 8), so store 0
+          // writes tokens 16 j + 0..7 and store 1 tokens 16 j + 8..15, each
+          // token's 64 channels (64 hf ..) by 8 lanes. Non-temporal stores of
+          // half lines cost about a third more bytes past the L2.
+          const bool lo = ir < 8;
+          v4u st0, st1;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t give = lo ? pk[1][q] : pk[0][q];
+            const uint32_t got =
+                (uint32_t)__builtin_amdgcn_update_dpp(0, (int)give, 0x128, 0xF, 0xF, false);
+            st0[q] = lo ? pk[0][q] : got;
+            st1[q] = lo ? got : pk[1][q];
+          }
+          // Rows past M (clamped tiles only) hold exactly row M-1's sums
+          // (their loads were clamped to it) and its scale, so they store row
+          // M-1's values to row M-1: every lane issues its stores and the
+          // per-tile store count stays fixed.
+          int m_st0 = m0 + wm * (16 * kTM) + 16 * j + (ir & 7), m_st1 = m_st0 + 8;
+          if constexpr (!kFull) {
+            m_st0 = m_st0 < M ? m_st0 : M - 1;
+            m_st1 = m_st1 < M ? m_st1 : M - 1;
+          }
+          const int col = n_wave + 64 * hf + 32 * (ir >> 3) + 8 * kq;
+          // Non-temporal: the output streams past the caches instead of
+          // evicting the activation and weight rows the next tiles read.
+          __builtin_nontemporal_store(st0, reinterpret_cast<v4u*>(o + (int64_t)m_st0 * ldo + col));
+          __builtin_nontemporal_store(st1, reinterpret_cast<v4u*>(o + (int64_t)m_st1 * ldo + col));
         }
       }
     }
