@@ -93,14 +93,17 @@ __device__ __forceinline__ uint32_t gelu_index(uint32_t bits) {
   return c + (bits >> 15) * (uint32_t)kGeluHalf;
 }
 
-// One BF16 GELU (bits in, bits out) given the table entry t read for it.
+// One BF16 GELU (bits in the low half, high half zero; bits out the same
+// way) given the table entry t read for it.
 __device__ __forceinline__ uint32_t gelu_select(uint32_t bits, uint32_t t) {
   const uint32_t a = bits & 0x7FFFu;
   const uint32_t idx = a - kGeluLow;
-  const uint32_t half = pack_bf16x2(__uint_as_float(bits << 16) * 0.5f, 0.0f) & 0xFFFFu;
-  const bool neg = (bits >> 15) != 0;
-  // e >= 131: finite -> y or -0; +inf -> +inf; -inf -> NaN; NaN -> itself
-  const uint32_t far = a < 0x7F80u ? (neg ? 0x8000u : bits) : (bits == 0xFF80u ? 0xFFC0u : bits);
+  // the high half of the packed pair is the BF16 of +0, all zero bits
+  const uint32_t half = pack_bf16x2(__uint_as_float(bits << 16) * 0.5f, 0.0f);
+  // e >= 131: positive y (+inf included) -> y; negative finite -> -0;
+  // -inf -> NaN (0xFFC0); NaN stays NaN (its quiet bit set)
+  const uint32_t far_neg = a >= 0x7F80u ? (bits | 0x40u) : 0x8000u;
+  const uint32_t far = bits >= 0x8000u ? far_neg : bits;
   return idx < (uint32_t)kGeluHalf ? t : (a < kGeluLow ? half : far);
 }
 
@@ -380,16 +383,17 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
                 v[2 * q + 1] = v[2 * q + 1] + bf16_hi(bw[4 * pp + q]);
               }
             }
-            v4u packed{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                       pack_bf16x2(v[6], v[7])};
+            v4u packed;
             if constexpr (kGelu) {   // the FFN activation on the BF16 Linear output
+              // each value rounded to BF16 on its own (bits in the low half)
+              uint32_t y[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) y[e] = pack_bf16x2(v[e], 0.0f);
               const uint32_t tab = lds_addr(gelu_lds);
               uint32_t t[8];
 #pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const uint32_t bits = (packed[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                asm volatile("ds_read_u16 %0, %1" : "=v"(t[e]) : "v"(tab + 2 * gelu_index(bits)));
-              }
+              for (int e = 0; e < 8; ++e)
+                asm volatile("ds_read_u16 %0, %1" : "=v"(t[e]) : "v"(tab + 2 * gelu_index(y[e])));
               asm volatile("s_waitcnt lgkmcnt(0)"
                            : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]),
                              "+v"(t[5]), "+v"(t[6]), "+v"(t[7])
@@ -397,8 +401,11 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
                            : "memory");
 #pragma unroll
               for (int q = 0; q < 4; ++q)
-                packed[q] = gelu_select(packed[q] & 0xFFFFu, t[2 * q]) |
-                            (gelu_select(packed[q] >> 16, t[2 * q + 1]) << 16);
+                packed[q] = gelu_select(y[2 * q], t[2 * q]) |
+                            (gelu_select(y[2 * q + 1], t[2 * q + 1]) << 16);
+            } else {
+              packed = v4u{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                           pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
             }
             pk[pp] = packed;
           }
