@@ -64,10 +64,10 @@ hipError_t launch_splitk_postscale(const int32_t* ws, int splits, int64_t M, int
                                    hipStream_t st);
 
 // K parts for a post-scale GEMM of this shape on `cus` compute units, from a
-// cost model of the split (fewer stages per work item against the partial
-// sums' HBM traffic and a fixed cost); 1 unless splitting saves a quarter of
-// the time. The W8A8_SPLIT_K environment variable overrides it (1 disables
-// splitting).
+// cost model of the split (fewer stages per work item against a per-item
+// cost, the partial sums' traffic, a fixed cost and the host's floor); 1
+// unless splitting saves 15% of the time. The W8A8_SPLIT_K environment
+// variable overrides it (1 disables splitting).
 int splitk_parts(int64_t M, int64_t N, int64_t K, int cus);
 
 // Persistent pipelined kernel with per-K-block scales.
