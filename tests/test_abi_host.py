@@ -253,6 +253,11 @@ def test_splitk_parts_query():
     assert w8.splitk_parts(28672, 16384, 4096) == 1          # tiles fill the chip
     assert w8.splitk_parts(1000, 5120, 5120) == 1            # partial sums would cost more
     assert w8.splitk_parts(129, 5120, 13824) > 1
+    # the cost model's measured calls: split where a sweep on MI355X showed a
+    # saving (512 x 4096 x 4096: 35 against 42 us), not where it showed none
+    assert w8.splitk_parts(512, 4096, 4096) > 1
+    assert w8.splitk_parts(1024, 4096, 4096) == 1 and w8.splitk_parts(256, 16384, 4096) == 1
+    assert 4 <= w8.splitk_parts(256, 5120, 13824) <= 16
     assert w8.splitk_parts(0, 128, 256) == 1 and w8.splitk_parts(4, 128, 0) == 1
     for M, N, K in ((1, 256, 2048), (256, 5120, 13824), (33, 128, 8192)):
         p = w8.splitk_parts(M, N, K)

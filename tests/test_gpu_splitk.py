@@ -24,12 +24,12 @@ pytestmark = pytest.mark.gpu
 # splits K (parts in the comments, for 256 compute units): ragged and whole
 # tiles, parts of equal and unequal stage counts, one-stage parts
 SPLIT_SHAPES = [((129, 5120, 13824), 132),    # 9 parts of 12 stages
-                ((64, 1024, 4096), 134),      # 16 parts of 2
-                ((33, 128, 8192), 137),       # 64 parts of 1
-                ((1, 5120, 5120), 138),       # 10 parts of 4
-                ((100, 2048, 3200), 139),     # 9 parts of 2 or 3 stages
-                ((300, 768, 5248), 140),      # 11 parts of 3 or 4; full-tile mode
-                ((77, 384, 11136), 145),      # 44 parts of 1 or 2
+                ((64, 1024, 4096), 134),      # 4 parts of 8
+                ((33, 128, 8192), 137),       # 8 parts of 8
+                ((1, 5120, 5120), 138),       # 5 parts of 8
+                ((100, 2048, 3200), 139),     # 4 parts of 6 or 7 stages
+                ((300, 768, 5248), 140),      # 6 parts of 6 or 7; full-tile mode
+                ((77, 384, 11136), 145),      # 10 parts of 8 or 9
                 ((512, 1280, 8192), 146),     # 8 parts of 8; full-tile mode
                 # not split (the tiles fill the chip, or the partial sums cost
                 # more than they save): the single pass, same bar
@@ -75,3 +75,61 @@ def test_splitk_strided_output_and_repeat():
         torch.cuda.synchronize()
         assert np.array_equal(bf16_from_dev(full[:, :N]), ref)
         assert torch.all(full[:, N:] == -3.0)
+
+
+_FORCED_CHILD = r"""
+import sys
+import numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+import oracle as O
+import workloads as W
+import w8a8_int8_quantized_token_amd as w8
+dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+bad = 0
+# parts forced to 64, capped by the 128-byte K stages: one-stage parts, parts
+# of one or two stages, and as many parts as stages
+for (M, N, K, seed, want) in ((33, 128, 8192, 171, 64), (77, 384, 11136, 172, 64),
+                              (300, 768, 5248, 173, 41), (256, 512, 2048, 174, 16)):
+    assert w8.splitk_parts(M, N, K) == want, (M, N, K, w8.splitk_parts(M, N, K))
+    qa = W.random_int8((M, K), seed)
+    qw = W.random_int8((N, K), seed + 1)
+    qa[1] = 127
+    qw[:4] = 127
+    sa = W.random_scales((M,), seed + 2)
+    sw = W.random_scales((N,), seed + 3, lo=1e-5, hi=1e-3)
+    b = W.random_bits((N,), seed + 4, std=0.5)
+    for bias, gelu in ((None, False), (b, False), (b, True)):
+        out = w8.w8a8_gemm_postscale(dev(qa), dev(qw), dev(sa), dev(sw),
+                                     bias=None if bias is None else torch.from_numpy(np.ascontiguousarray(bias).view(np.int16)).view(torch.bfloat16).cuda(),
+                                     gelu=gelu)
+        torch.cuda.synchronize()
+        got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        acc = O.gemm_i32(qa, qw)
+        if gelu:
+            ref = O.postscale_gelu_bf16(acc, sa, sw, bias)
+        elif bias is None:
+            ref = O.postscale_bf16(acc, sa, sw)
+        else:
+            ref = O.postscale_bias_bf16(acc, sa, sw, bias)
+        n = int(np.count_nonzero(got != ref))
+        print(f"{M}x{N}x{K} parts {want} bias={bias is not None} gelu={gelu}: {n} mismatches", flush=True)
+        bad += n
+sys.exit(0 if bad == 0 else 1)
+"""
+
+
+def test_splitk_forced_parts_exact():
+    """Many small parts (W8A8_SPLIT_K=64, capped by the K stages), which the cost
+    model no longer picks: one-stage parts, parts of unequal length, full-tile
+    mode, with bias and GELU epilogues; in a child process because the variable
+    is read once per process."""
+    import os
+    import subprocess
+    import sys
+    log("split-K with forced parts (child process)")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _FORCED_CHILD, root], capture_output=True,
+                       text=True, timeout=240, env={**os.environ, "W8A8_SPLIT_K": "64"})
+    for line in r.stdout.strip().splitlines():
+        log("  " + line)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
