@@ -262,7 +262,10 @@ GEMM_SHAPES = [((64, 128, 256), 51), ((1, 128, 128), 52), ((1000, 384, 512), 53)
                # more tiles than CUs: several tiles per persistent workgroup
                ((4096, 16384, 256), 59), ((8292, 4096, 128), 60), ((2000, 3200, 384), 66),
                # one whole tile; one row short of it (clamped loads)
-               ((256, 256, 256), 80), ((255, 4096, 512), 81)]
+               ((256, 256, 256), 80), ((255, 4096, 512), 81),
+               # fewer than 16 tokens: clamped rows on one or both sides of the
+               # store's swap between lanes 8 rows apart
+               ((7, 256, 256), 82), ((9, 384, 128), 83), ((15, 1280, 384), 84)]
 
 
 @pytest.mark.parametrize("shape,seed", GEMM_SHAPES)
