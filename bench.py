@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calib", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
+    p.add_argument("--no-ceiling", action="store_true",
+                   help="skip the main-loop ceiling probe in the bench line's extra fields")
     p.add_argument("--ceiling", action="store_true",
                    help="only time the post-scale GEMM's main loop alone (probe library) on "
                         "constant and on random operands")
@@ -83,17 +85,18 @@ def copy_calibration(steps: int) -> None:
                       "copy_gbs": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
-def mainloop_ceiling() -> None:
+def measure_mainloop_ceiling(verbose: bool = False):
     """The post-scale GEMM's inner loop alone (libw8a8_probe.so: the same LDS
     ring, fragment reads and MFMA stream, no epilogue, operands L2-resident),
     timed on constant operands, on uniformly random ones, and on random ones
     without the stage refills. The first is the rate the schedule allows; the
-    drop to the second is what the power drawn by random operands costs."""
+    drop to the second is what the power drawn by random operands costs.
+    Returns {case: {...}} or None if the probe library is not built."""
     import ctypes
     import torch
     path = os.path.join(ROOT, "w8a8_int8_quantized_token_amd", "libw8a8_probe.so")
     if not os.path.exists(path):
-        sys.exit("libw8a8_probe.so is missing: build it with __graft_entry__.build()")
+        return None
     lib = ctypes.CDLL(path)
     lib.w8a8_probe_mainloop_workgroups.restype = ctypes.c_int
     lib.w8a8_probe_mainloop.restype = ctypes.c_int
@@ -103,7 +106,7 @@ def mainloop_ceiling() -> None:
     torch.cuda.init()
     grid = lib.w8a8_probe_mainloop_workgroups()
     if grid < 1:
-        sys.exit("cannot read the compute-unit count")
+        raise RuntimeError("cannot read the compute-unit count")
     src = torch.empty(2 << 20, dtype=torch.int8, device="cuda")
     sink = torch.empty(grid * 512, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
@@ -123,7 +126,7 @@ def mainloop_ceiling() -> None:
             rc = lib.w8a8_probe_mainloop(src.data_ptr(), src.numel(), stages, refill,
                                          sink.data_ptr(), sink.numel(), stream.cuda_stream)
             if rc != 0:
-                sys.exit(f"w8a8_probe_mainloop failed ({rc})")
+                raise RuntimeError(f"w8a8_probe_mainloop failed ({rc})")
 
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         call()
@@ -145,10 +148,18 @@ def mainloop_ceiling() -> None:
                          "us_per_stage": round(ms * 1e3 / stages, 4),
                          "tops": round(ops / (ms * 1e-3) / 1e12, 1),
                          "frac_of_int8_peak": round(ops / (ms * 1e-3) / 5.0e15, 4)}
-        print(f"{name:18s} {results[name]}", flush=True)
-    print(json.dumps({"probe": "gemm_mainloop", "workgroups": grid, "stages": stages,
-                      "block_tile": [256, 256, 128], "peak_tops": 5000.0,
-                      "results": results}), flush=True)
+        if verbose:
+            print(f"{name:18s} {results[name]}", flush=True)
+    return {"workgroups": grid, "stages": stages, "results": results}
+
+
+def mainloop_ceiling() -> None:
+    res = measure_mainloop_ceiling(verbose=True)
+    if res is None:
+        sys.exit("libw8a8_probe.so is missing: build it with __graft_entry__.build()")
+    print(json.dumps({"probe": "gemm_mainloop", "workgroups": res["workgroups"],
+                      "stages": res["stages"], "block_tile": [256, 256, 128],
+                      "peak_tops": 5000.0, "results": res["results"]}), flush=True)
 
 
 def source_hash(*names) -> str:
@@ -334,6 +345,20 @@ def main():
         bf16_ms = e0.elapsed_time(e1) / reps
         extra["torch_bf16_linear_ms"] = round(bf16_ms, 4)
         extra["speedup_vs_bf16_linear"] = round(bf16_ms / float(step_ms.mean()), 3)
+
+    # ---- the post-scale kernel's own main loop on this GPU, as a yardstick
+    # for roofline.frac (the chip's power limit caps it on random operands) --
+    if gemm_name.startswith("gemm_postscale") and not args.no_ceiling:
+        try:
+            ceil = measure_mainloop_ceiling()
+        except RuntimeError as e:     # the probe is a yardstick, not the product
+            ceil = None
+            extra["mainloop_ceiling_error"] = str(e)
+        if ceil is not None:
+            fr = {k: v["frac_of_int8_peak"] for k, v in ceil["results"].items()}
+            extra["mainloop_ceiling_frac"] = fr
+            extra["gemm_frac_of_mainloop_ceiling_random"] = round(
+                gemm_tops / INT8_PEAK_TOPS / fr["random"], 4)
 
     # ---- CPU oracle on a bounded sample of the same workload -----------------
     cpu = None
