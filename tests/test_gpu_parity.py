@@ -393,3 +393,26 @@ def test_tiny_linear_end_to_end():
     ref, qa_o, sa_o, qw_o, sw_o, acc = O.w8a8_linear(x, wb)
     assert np.array_equal(from_dev(qa), qa_o) and np.array_equal(from_dev(qw), qw_o)
     ulp_report(bf16_from_dev(out), ref, "tiny linear")
+
+
+def test_max_k_int32_extremes():
+    """K = W8A8_MAX_K (133120, the largest multiple of 128 with 127^2 K < 2^31):
+    rows of +127 and -127 against rows of +127 and -127 reach the INT32
+    extremes +-2147123200 exactly, through the INT32 export (one pass over the
+    whole K) and the post-scale path (split over K at this size)."""
+    M, N, K = 16, 128, w8.W8A8_MAX_K
+    log(f"K = W8A8_MAX_K: {M}x{N}x{K}, split-K parts {w8.splitk_parts(M, N, K)}")
+    qa = W.random_int8((M, K), 201)
+    qw = W.random_int8((N, K), 202)
+    qa[0], qa[1] = 127, -127
+    qw[0], qw[1] = 127, -127
+    sa = W.random_scales((M,), 203)
+    sw = W.random_scales((N,), 204, lo=1e-5, hi=1e-3)
+    ref = O.gemm_i32(qa, qw)
+    assert ref[0, 0] == 127 * 127 * K and ref[1, 0] == -127 * 127 * K and ref[1, 1] == 127 * 127 * K
+    got = from_dev(w8.w8a8_gemm_i32(to_dev(qa), to_dev(qw)))
+    sync()
+    assert np.array_equal(got, ref)
+    out = w8.w8a8_gemm_postscale(to_dev(qa), to_dev(qw), to_dev(sa), to_dev(sw))
+    sync()
+    assert np.array_equal(bf16_from_dev(out), O.postscale_bf16(ref, sa, sw))
