@@ -199,7 +199,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the W8A8 Linear is "
-              "token-parallel and needs no collectives; see DESIGN.md for how it would shard.",
+              "token-parallel and needs no collectives (several GPUs would each take their own token "
+              "rows, with the quantised weight replicated).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -300,3 +300,11 @@ def test_probe_library_loads_and_rejects_bad_arguments():
     assert f(1 << 20, (2 << 20) - 1, 8, 1, 1 << 20, 1 << 20, None) == 1   # buffer too small
     assert f(1 << 20, 2 << 20, 0, 1, 1 << 20, 1 << 20, None) == 1    # no stages
     assert f(1 << 20, 2 << 20, 8, 2, 1 << 20, 1 << 20, None) == 1    # refill not 0/1
+
+
+def test_bench_refuses_several_gpus():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU only" in r.stderr
