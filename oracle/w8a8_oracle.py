@@ -15,7 +15,7 @@ What the method computes, per the pages:
   fused implementation; here it is the optional prologue of the activation
   quantisation.
 
-Readings taken where the pages are silent (each one is listed in the design doc):
+Readings taken where the pages are silent:
 
 R1  scale = absmax / 127, symmetric, no zero point, stored as fp32.
 R2  code = round-half-even(fl32(x / scale)), clamped to [-127, 127]. The
