@@ -72,6 +72,11 @@ def short_name(kernel: str) -> str:
         return "quant_block128"
     if "copyBuffer" in kernel:
         return "hip_copy_buffer"
+    if "mainloop<" in kernel:
+        # the GEMM main-loop ceiling probe the default bench line also runs
+        return "probe_mainloop_norefill" if "mainloop<false>" in kernel else "probe_mainloop"
+    if "at::native" in kernel:
+        return "torch_" + ("fill" if "FillFunctor" in kernel else "elementwise")
     return kernel.split("(")[0][-40:]
 
 

@@ -58,7 +58,7 @@ constexpr int kScaleBytes = (kBN + kBM) * 4;   // one tile's scales
 constexpr int kBiasBytes = kWaves * 256;       // one dword wave-load per wave (the tile's
                                                // 256 BF16 biases fill the first 512 bytes)
 constexpr int kScaleBufs = 3;                  // tile k's scales sit in buffer k % 3
-constexpr int kGroupM = 8;
+constexpr int kGroupM = 4;
 
 // GELU of a BF16 value y (to BF16), by ranges of its exponent field e:
 //  * e <= 117 (|y| < 2^-9): GELU(y) rounds to the BF16 rounding of y/2
