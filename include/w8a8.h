@@ -16,9 +16,9 @@
  *
  * Conventions shared by every entry point:
  *   - Every data pointer is a DEVICE pointer, owned by the caller. The library
- *     keeps no state between calls and never synchronises. It allocates
- *     nothing, except the split-K workspace of the post-scale GEMMs (see
- *     w8a8_gemm_postscale), which is stream-ordered on the caller's stream.
+ *     keeps no state between calls, never synchronises and allocates nothing:
+ *     scratch memory (the split-K workspace of w8a8_gemm_postscale_ex) is the
+ *     caller's. What a call does is fixed by its arguments and the device.
  *   - Row-major layouts; leading dimensions (ld*) are in ELEMENTS.
  *   - BF16 values travel as their 16-bit patterns (uint16_t).
  *   - `stream` is a hipStream_t passed as an opaque pointer (NULL = the
@@ -172,15 +172,10 @@ w8a8_status_t w8a8_layernorm_quant(const uint16_t* x, const uint16_t* gamma,
  * W8A8_MAX_K, N % 128 == 0; a, w, out 16-byte aligned; lda % 16 == 0,
  * ldw % 16 == 0, ldo % 8 == 0; scales 4-byte aligned. M >= 0 arbitrary.
  *
- * Split-K: when the 256 x 256 output tiles would leave most compute units
- * idle (few tokens, long K) the call cuts K into parts
- * (w8a8_gemm_splitk_parts), writes their exact INT32 partial sums to a
- * workspace taken with hipMallocAsync on `stream` (parts * M * N * 4 bytes,
- * at most 1 GiB) and released with hipFreeAsync on it after one more pass
- * adds them and applies this epilogue. The output is bit-identical to the
- * single pass. If the workspace cannot be had the single pass runs. The
- * environment variable W8A8_SPLIT_K=1 disables splitting (=n forces n parts).
- * The same holds for w8a8_gemm_postscale_bias and w8a8_gemm_postscale_gelu.
+ * This entry point always runs the single pass (one kernel). When the
+ * 256 x 256 output tiles would leave most compute units idle (few tokens,
+ * long K), w8a8_gemm_postscale_ex can split K over a caller-provided
+ * workspace instead.
  */
 w8a8_status_t w8a8_gemm_postscale(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
                                   const float* a_scale, const float* w_scale,
@@ -231,6 +226,54 @@ w8a8_status_t w8a8_gemm_postscale_gelu(const int8_t* a, int64_t lda, const int8_
                                        const uint16_t* bias, uint16_t* out, int64_t ldo,
                                        int64_t M, int64_t N, int64_t K, void* stream);
 
+/* Epilogue flag of w8a8_gemm_postscale_ex: GELU (erf form) of the BF16 output,
+   as w8a8_gemm_postscale_gelu. */
+#define W8A8_EPILOGUE_GELU 1
+
+/*
+ * w8a8_gemm_postscale_ex -- the post-scale GEMM family (optional bias,
+ * optional GELU) with split-K over a caller-provided workspace.
+ *
+ * Passage: "Differences From TurboDiffusion", paragraph under the table: one
+ * INT32 accumulation over all of K, the scales applied in the epilogue.
+ * Integer addition is exact and associative, so K may be cut into parts whose
+ * exact INT32 partial sums add up to exactly the full sum; the output is then
+ * bit-identical to the single pass.
+ *
+ *   bias            [N] BF16, 16-byte aligned, or NULL (none)
+ *   flags           0 or W8A8_EPILOGUE_GELU; other bits are
+ *                   W8A8_ERR_INVALID_ARGUMENT
+ *   parts           0: the library's choice for this shape and device
+ *                   (w8a8_gemm_splitk_parts); 1: single pass; 2..64 (and at
+ *                   most K / 128): exactly that many K parts
+ *   workspace       device memory of workspace_bytes bytes, 16-byte aligned,
+ *                   owned by the caller, or NULL. Split-K writes
+ *                   parts * M * N INT32 partial sums there (the size
+ *                   w8a8_gemm_postscale_workspace_size reports); it must not
+ *                   overlap any input or the output, and must not be used by
+ *                   other work until this call's work on `stream` is done.
+ * With parts == 0 and no workspace the call runs the single pass. Asking for
+ * parts > 1 without a workspace, or a workspace smaller than it needs, is
+ * W8A8_ERR_INVALID_ARGUMENT. Everything else, requirements and errors as
+ * w8a8_gemm_postscale (bias) and w8a8_gemm_postscale_gelu (flags).
+ */
+w8a8_status_t w8a8_gemm_postscale_ex(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
+                                     const float* a_scale, const float* w_scale,
+                                     const uint16_t* bias, int32_t flags,
+                                     uint16_t* out, int64_t ldo,
+                                     int64_t M, int64_t N, int64_t K,
+                                     int32_t parts, void* workspace, int64_t workspace_bytes,
+                                     void* stream);
+
+/*
+ * w8a8_gemm_postscale_workspace_size -- bytes of workspace w8a8_gemm_postscale_ex
+ * needs for an M x N x K GEMM with `parts` (0 = the library's choice) on the
+ * current device: parts * M * N * 4 when it splits K, 0 for the single pass,
+ * -1 for arguments w8a8_gemm_postscale_ex would reject (a shape outside the
+ * INT8 path, parts out of range). Host only, launches nothing.
+ */
+int64_t w8a8_gemm_postscale_workspace_size(int64_t M, int64_t N, int64_t K, int32_t parts);
+
 /*
  * w8a8_gemm_blockwise -- blockwise-scaled W8A8 GEMM (the original
  * TurboDiffusion scheme, "Differences From TurboDiffusion", W8A8 kernel row).
@@ -268,13 +311,13 @@ const char* w8a8_last_error(void);
 const char* w8a8_version(void);
 
 /*
- * w8a8_gemm_splitk_parts -- how many K parts the post-scale entry points
- * (w8a8_gemm_postscale, _bias, _gelu) use for an M x N x K GEMM on the current
- * device: 1 for a single pass, else the parts of the split-K path (exact INT32
- * partial sums in a stream-ordered workspace of parts * M * N * 4 bytes, then
- * one epilogue pass). Host only, launches nothing. Passage: "Differences From
- * TurboDiffusion", paragraph under the table (one INT32 accumulation over K;
- * integer sums may be formed in parts and added exactly).
+ * w8a8_gemm_splitk_parts -- how many K parts w8a8_gemm_postscale_ex chooses
+ * (parts == 0) for an M x N x K GEMM on the current device: 1 for a single
+ * pass, else the parts of the split-K path (exact INT32 partial sums in the
+ * caller's workspace of parts * M * N * 4 bytes, then one epilogue pass).
+ * Host only, launches nothing. Passage: "Differences From TurboDiffusion",
+ * paragraph under the table (one INT32 accumulation over K; integer sums may
+ * be formed in parts and added exactly).
  */
 int32_t w8a8_gemm_splitk_parts(int64_t M, int64_t N, int64_t K);
 

@@ -38,7 +38,8 @@ def test_library_exports_every_declared_symbol():
                           "w8a8_gemm_postscale", "w8a8_gemm_postscale_bias",
                           "w8a8_gemm_postscale_gelu",
                           "w8a8_gemm_blockwise", "w8a8_gemm_i32", "w8a8_status_string",
-                          "w8a8_last_error", "w8a8_version", "w8a8_gemm_splitk_parts"}
+                          "w8a8_last_error", "w8a8_version", "w8a8_gemm_splitk_parts",
+                          "w8a8_gemm_postscale_ex", "w8a8_gemm_postscale_workspace_size"}
     raw = ctypes.CDLL(w8.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -140,6 +141,8 @@ def gemm(fn="w8a8_gemm_postscale", a=P, lda=256, w=Q, ldw=256, sa=S, sw=S + 0x10
         return f(a, lda, w, ldw, sa, sw, S + 0x200000, out, ldo, M, N, K, None)
     if fn == "w8a8_gemm_i32":
         return f(a, lda, w, ldw, out, ldo, M, N, K, None)
+    if fn == "w8a8_gemm_postscale_ex":
+        return f(a, lda, w, ldw, sa, sw, None, 0, out, ldo, M, N, K, 1, None, 0, None)
     return f(a, lda, w, ldw, sa, sw, out, ldo, M, N, K, None)
 
 
@@ -165,7 +168,8 @@ GEMM_CASES = [
 
 @pytest.mark.parametrize("kwargs,status", GEMM_CASES)
 @pytest.mark.parametrize("fn", ["w8a8_gemm_postscale", "w8a8_gemm_postscale_bias",
-                                "w8a8_gemm_postscale_gelu", "w8a8_gemm_blockwise"])
+                                "w8a8_gemm_postscale_gelu", "w8a8_gemm_postscale_ex",
+                                "w8a8_gemm_blockwise"])
 def test_gemm_rejects(fn, kwargs, status):
     assert gemm(fn, **kwargs) == status
 
@@ -264,26 +268,122 @@ def test_splitk_parts_query():
         assert 1 <= p <= K // 128 and p * M * N * 4 <= 1 << 30
 
 
-@pytest.mark.parametrize("env", ["1", "5", "0"])
-def test_splitk_env_override(env):
-    # W8A8_SPLIT_K is read once per process, so each setting runs in a child
-    # (host only: the query launches nothing).  An override is still capped by
-    # the number of 128-byte K stages and by the 1 GiB workspace limit.
-    import subprocess
-    import sys
-    shapes = [(129, 5120, 13824), (2048, 4096, 4096), (129, 5120, 256), (28672, 16384, 4096)]
-    code = ("import w8a8_int8_quantized_token_amd as w8; "
-            f"print(*[w8.splitk_parts(*s) for s in {shapes!r}])")
-    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
-                       env={**os.environ, "W8A8_SPLIT_K": env}, timeout=120)
-    assert r.returncode == 0, r.stderr
-    small, mid, short_k, huge = map(int, r.stdout.split())
-    assert huge == 1                       # one part alone is 1.9 GB of INT32 partial sums
-    if env == "0":                         # not an override: the cost model decides
-        assert small > 1 and mid == 1 and short_k == 1
-    else:
-        f = int(env)
-        assert small == f and mid == f and short_k == min(f, 256 // 128)
+def test_workspace_size_query():
+    # parts = 0: the library's choice (no GPU here: the 256-unit default)
+    for M, N, K in ((256, 5120, 13824), (129, 5120, 13824), (28672, 16384, 4096)):
+        p = w8.splitk_parts(M, N, K)
+        assert w8.postscale_workspace_size(M, N, K) == (p * M * N * 4 if p > 1 else 0)
+    # forced parts, the single pass, and arguments the entry point would reject
+    assert w8.postscale_workspace_size(256, 5120, 13824, 3) == 3 * 256 * 5120 * 4
+    assert w8.postscale_workspace_size(256, 5120, 13824, 1) == 0
+    assert w8.postscale_workspace_size(0, 5120, 13824, 4) == 0
+    assert w8.postscale_workspace_size(64, 128, 256, 2) == 2 * 64 * 128 * 4
+    assert w8.postscale_workspace_size(64, 128, 256, 3) == -1          # more parts than stages
+    assert w8.postscale_workspace_size(64, 128, 256 * 64, 65) == -1    # more than 64 parts
+    assert w8.postscale_workspace_size(64, 128, 256, -1) == -1
+    assert w8.postscale_workspace_size(64, 100, 256, 0) == -1          # N % 128
+    assert w8.postscale_workspace_size(64, 128, 200, 0) == -1          # K % 128
+    assert w8.postscale_workspace_size(-1, 128, 256, 0) == -1
+
+
+WS = 0x70000000          # fake workspace address
+
+
+def ex(parts=2, ws=WS, ws_bytes=1 << 20, flags=0, bias=None, out=O, M=64, N=128, K=256):
+    return w8.lib().w8a8_gemm_postscale_ex(P, 256, Q, 256, S, S + 0x100000, bias, flags, out, N,
+                                           M, N, K, parts, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(flags=2), INVALID),                               # unknown epilogue flag
+    (dict(parts=-1), INVALID),
+    (dict(parts=65, K=65 * 128), INVALID),                  # more than 64 parts
+    (dict(parts=3), INVALID),                               # more parts than K stages (2)
+    (dict(ws=None, ws_bytes=0), INVALID),                   # forced split without workspace
+    (dict(ws_bytes=2 * 64 * 128 * 4 - 4), INVALID),         # workspace too small
+    (dict(ws_bytes=-1), INVALID),
+    (dict(ws=WS + 8), UNSUPPORTED),                         # workspace not 16-byte aligned
+    (dict(ws=O + 0x100), INVALID),                          # workspace inside the output
+    (dict(ws=Q - 0x100), INVALID),                          # workspace runs into w
+    (dict(ws=S - 0x100), INVALID),                          # workspace runs into a_scale
+    (dict(bias=S + 0x200008), UNSUPPORTED),                 # bias not 16-byte aligned
+])
+def test_postscale_ex_rejects(kwargs, status):
+    assert ex(**kwargs) == status
+    assert w8.lib().w8a8_last_error() != b""
+
+
+def test_postscale_ex_empty_call_is_noop():
+    # zero rows: nothing to split, no workspace needed
+    assert ex(parts=2, ws=None, ws_bytes=0, M=0) == OK
+    assert ex(parts=3, M=0) == INVALID          # the parts rule still applies
+
+
+# The binding checks every buffer against the call's shape before anything
+# reaches the library (which sees bare pointers). Host tensors reach the
+# shape checks first, so these run without a GPU.
+
+def _bf(*shape):
+    return torch.zeros(*shape, dtype=torch.bfloat16)
+
+
+def _i8(*shape):
+    return torch.zeros(*shape, dtype=torch.int8)
+
+
+def _f32(*shape):
+    return torch.zeros(*shape, dtype=torch.float32)
+
+
+@pytest.mark.parametrize("call,what", [
+    (lambda: w8.w8a8_quant_rows(_bf(4, 256), q=_i8(3, 256)), "q must have shape"),
+    (lambda: w8.w8a8_quant_rows(_bf(4, 256), q=_i8(4, 128)), "q must have shape"),
+    (lambda: w8.w8a8_quant_rows(_bf(4, 256), scale=_f32(3)), "scale must be contiguous with 4"),
+    (lambda: w8.w8a8_quant_rows(_bf(4, 256), 1, 128, scale=_f32(4)), "with 8 elements"),
+    (lambda: w8.w8a8_quant_rows(_bf(200, 256), 128, 128, scale=_f32(2)), "with 4 elements"),
+    (lambda: w8.w8a8_quant_rows(_bf(4, 256), scale=_bf(4)), "scale must be a torch.float32"),
+    (lambda: w8.w8a8_rmsnorm_quant(_bf(4, 256), _bf(255)), "gamma"),
+    (lambda: w8.w8a8_rmsnorm_quant(_bf(4, 256), _bf(256), inv_rms=_f32(3)), "inv_rms"),
+    (lambda: w8.w8a8_rmsnorm_quant(_bf(4, 256), _bf(256), scale=_f32(5)), "scale"),
+    (lambda: w8.w8a8_layernorm_quant(_bf(4, 256), mean=_f32(3)), "mean"),
+    (lambda: w8.w8a8_layernorm_quant(_bf(4, 256), rstd=_f32(2)), "rstd"),
+    (lambda: w8.w8a8_layernorm_quant(_bf(4, 256), mod_shift=_bf(128)), "mod_shift"),
+    (lambda: w8.w8a8_layernorm_quant(_bf(4, 256), q=_i8(4, 255)), "q must have shape"),
+    (lambda: w8.w8a8_gemm_postscale(_i8(64, 256), _i8(128, 256), _f32(64), _f32(128),
+                                    out=_bf(63, 128)), "out must have shape (64, 128)"),
+    (lambda: w8.w8a8_gemm_postscale(_i8(64, 256), _i8(128, 256), _f32(64), _f32(128),
+                                    out=_bf(64, 256)[:, :127]), "out must have shape"),
+    (lambda: w8.w8a8_gemm_postscale(_i8(64, 256), _i8(128, 256), _f32(63), _f32(128)),
+     "a_scale must be contiguous with 64"),
+    (lambda: w8.w8a8_gemm_postscale(_i8(64, 256), _i8(128, 256), _f32(64), _f32(127)),
+     "w_scale must be contiguous with 128"),
+    (lambda: w8.w8a8_gemm_postscale(_i8(64, 256), _i8(128, 256), _f32(64), _bf(128)),
+     "w_scale must be a torch.float32"),
+    (lambda: w8.w8a8_gemm_postscale(_i8(64, 256), _i8(128, 256), _f32(64), _f32(128),
+                                    bias=_bf(64)), "bias"),
+    (lambda: w8.w8a8_gemm_postscale(_i8(64, 256), _i8(128, 128), _f32(64), _f32(128)),
+     "K mismatch"),
+    (lambda: w8.w8a8_gemm_blockwise(_i8(64, 256), _i8(128, 256), _f32(64, 1), _f32(1, 2)),
+     "a_scale must be contiguous with 128"),
+    (lambda: w8.w8a8_gemm_blockwise(_i8(64, 256), _i8(128, 256), _f32(64, 2), _f32(1, 1)),
+     "w_scale must be contiguous with 2"),
+    (lambda: w8.w8a8_gemm_blockwise(_i8(64, 256), _i8(128, 256), _f32(64, 2), _f32(1, 2),
+                                    out=_bf(64, 64)), "out must have shape"),
+    (lambda: w8.w8a8_gemm_i32(_i8(64, 256), _i8(128, 256), out=torch.zeros(64, 64, dtype=torch.int32)),
+     "out must have shape"),
+])
+def test_binding_rejects_undersized_buffers(call, what):
+    with pytest.raises(w8.W8A8Error) as e:
+        call()
+    assert what in str(e.value), str(e.value)
+
+
+def test_binding_rejects_host_tensors_after_shape_checks():
+    # right shapes on the host: the device check is what fails
+    with pytest.raises(w8.W8A8Error, match="device tensor"):
+        w8.w8a8_gemm_postscale(_i8(64, 256), _i8(128, 256), _f32(64), _f32(128))
+    with pytest.raises(w8.W8A8Error, match="device tensor"):
+        w8.w8a8_rmsnorm_quant(_bf(4, 256), _bf(256))
 
 
 def test_probe_library_loads_and_rejects_bad_arguments():

@@ -7,8 +7,14 @@ activation quant or RMSNorm+quant, the GEMM). The oracle checks:
   * activation codes and scales: every element where the oracle finishes in
     a few seconds, else a seeded sample of rows plus every row of the ragged
     last tile;
-  * GEMM output: the sampled rows, recomputed by the oracle from the
-    oracle's own codes (which were just shown equal to the device's).
+  * GEMM output: the sampled rows (every row when M is small), recomputed by
+    the oracle from the oracle's own codes (which were just shown equal to the
+    device's), bit for bit.
+
+The GEMM is called exactly as bench.py calls it: the post-scale family
+through w8a8_gemm_postscale with the workload's bias and GELU and the
+library's own choice of K parts (small_m splits K; the others run the single
+pass in full-tile mode).
 """
 from __future__ import annotations
 
@@ -34,14 +40,14 @@ def sample_rows(M: int, seed: int) -> np.ndarray:
     return np.unique(np.concatenate([pick, tail, [0]]))
 
 
-def ulp_check(got, ref, what):
+def exact_check(got, ref, what):
     d = O.bf16_ulp_distance(got, ref)
-    log(f"  {what}: max ulp {int(d.max())}, 1-ulp count {int(np.sum(d == 1))} of {d.size}")
-    assert d.max() <= 1
+    log(f"  {what}: max ulp {int(d.max())}, differing {int(np.sum(d != 0))} of {d.size}")
+    assert np.array_equal(got, ref)
 
 
 @pytest.mark.parametrize("name", ["square", "up_proj", "down_proj", "blockwise_small",
-                                  "blockwise_large", "ln_up_proj"])
+                                  "blockwise_large", "ln_up_proj", "up_proj_gelu", "small_m"])
 def test_workload_full_size(name):
     wl = W.WORKLOADS[name]
     M, N, K = wl.M, wl.N, wl.K
@@ -75,10 +81,16 @@ def test_workload_full_size(name):
         qa, sa = w8.w8a8_quant_rows(xd, 1, 128)
     else:
         qa, sa = w8.w8a8_quant_rows(xd)
+    bias = W.bias_bits(wl) if wl.bias_std > 0 else None
     if wl.blockwise:
         out = w8.w8a8_gemm_blockwise(qa, qw, sa, sw)
     else:
-        out = w8.w8a8_gemm_postscale(qa, qw, sa, sw)
+        parts = w8.splitk_parts(M, N, K)
+        log(f"  post-scale GEMM: bias={bias is not None} gelu={wl.gelu} K parts {parts}")
+        if name == "small_m":
+            assert parts > 1
+        out = w8.w8a8_gemm_postscale(qa, qw, sa, sw, bias=None if bias is None else bf16_to_dev(bias),
+                                     gelu=wl.gelu)
     torch.cuda.synchronize()
     del xd
 
@@ -108,7 +120,7 @@ def test_workload_full_size(name):
 
     # ---- GEMM on sampled rows --------------------------------------------
     if rows.size == M:
-        grows = sample_rows(M, 11 + M)
+        grows = np.arange(M) if M <= 1024 else sample_rows(M, 11 + M)
         sel = grows
     else:
         grows = rows
@@ -117,5 +129,12 @@ def test_workload_full_size(name):
     if wl.blockwise:
         ref = O.gemm_blockwise_bf16(qa_o[sel], sa_o.reshape(rows.size, -1)[sel], qw_o, sw_o)
     else:
-        ref = O.postscale_bf16(O.gemm_i32(qa_o[sel], qw_o), sa_o.reshape(-1)[sel], sw_o)
-    ulp_check(got, ref, f"{name} output on {grows.size} rows")
+        acc = O.gemm_i32(qa_o[sel], qw_o)
+        sa_sel = sa_o.reshape(-1)[sel]
+        if wl.gelu:
+            ref = O.postscale_gelu_bf16(acc, sa_sel, sw_o, bias)
+        elif bias is not None:
+            ref = O.postscale_bias_bf16(acc, sa_sel, sw_o, bias)
+        else:
+            ref = O.postscale_bf16(acc, sa_sel, sw_o)
+    exact_check(got, ref, f"{name} output on {grows.size} rows")

@@ -56,46 +56,28 @@ def test_gelu_every_bf16_value():
     assert nan_in.sum() == 254 and np.all(np.isnan(g[nan_in]))
 
 
-_SPLIT_CHILD = r"""
-import sys
-import numpy as np, torch
-sys.path.insert(0, sys.argv[1])
-import oracle as O
-import w8a8_int8_quantized_token_amd as w8
-bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
-vals = O.bf16_to_f32(bits)
-finite = np.isfinite(vals)
-M, N, K = 65536, 128, 256
-assert w8.splitk_parts(M, N, K) == 2
-qa = np.zeros((M, K), np.int8); qa[:, 0] = 1
-qw = np.zeros((N, K), np.int8); qw[:, 0] = 1
-dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
-out = w8.w8a8_gemm_postscale(dev(qa), dev(qw), dev(vals.astype(np.float32)),
-                             dev(np.ones(N, np.float32)), gelu=True)
-torch.cuda.synchronize()
-got = out.view(torch.int16).cpu().numpy().view(np.uint16)
-assert np.all(got == got[:, :1])
-bad = int(np.count_nonzero(got[finite, 0] != O.gelu_bf16(bits[finite])))
-g = O.bf16_to_f32(got[:, 0])
-ok = bad == 0 and g[0x7F80] == np.inf and np.isnan(g[0xFF80]) and np.all(np.isnan(g[np.isnan(vals)]))
-print("split-K GELU mismatches", bad, "special values ok" if ok else "special values WRONG", flush=True)
-sys.exit(0 if ok else 1)
-"""
-
-
 def test_gelu_every_bf16_value_split_k():
     """The same over the split-K path, whose reduce pass computes GELU with
-    erfcf itself: forced to 2 parts (W8A8_SPLIT_K is read once per process,
-    so this runs in a child process)."""
-    import os
-    import subprocess
-    import sys
-    log("GELU in the split-K reduce pass over all 65536 BF16 patterns (child process)")
-    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    r = subprocess.run([sys.executable, "-c", _SPLIT_CHILD, root], capture_output=True,
-                       text=True, timeout=240, env={**os.environ, "W8A8_SPLIT_K": "2"})
-    log("  " + (r.stdout.strip() or r.stderr.strip()[-400:]))
-    assert r.returncode == 0, r.stdout + r.stderr[-2000:]
+    erfcf itself: forced to 2 parts."""
+    log("GELU in the split-K reduce pass over all 65536 BF16 patterns")
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = O.bf16_to_f32(bits)
+    finite = np.isfinite(vals)
+    M, N, K = 65536, 128, 256
+    qa = np.zeros((M, K), np.int8)
+    qa[:, 0] = 1
+    qw = np.zeros((N, K), np.int8)
+    qw[:, 0] = 1
+    out = w8.w8a8_gemm_postscale(to_dev(qa), to_dev(qw), to_dev(vals.astype(np.float32)),
+                                 to_dev(np.ones(N, np.float32)), gelu=True, parts=2)
+    torch.cuda.synchronize()
+    got = bf16_from_dev(out)
+    assert np.all(got == got[:, :1])
+    bad = int(np.count_nonzero(got[finite, 0] != O.gelu_bf16(bits[finite])))
+    g = O.bf16_to_f32(got[:, 0])
+    log(f"  split-K GELU mismatches {bad}")
+    assert bad == 0
+    assert g[0x7F80] == np.inf and np.isnan(g[0xFF80]) and np.all(np.isnan(g[np.isnan(vals)]))
 
 
 SHAPES = [((64, 128, 256), 151), ((1000, 384, 512), 152), ((257, 640, 1024), 153),

@@ -1,9 +1,11 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
-Bars: INT8 codes, fp32 scales and INT32 accumulators bit-exact; BF16 outputs
-within 1 BF16 ulp (the kernels perform the same fp32 operations in the same
-order as the oracle, so the count of 1-ulp differences is also reported and
-expected to be 0). RMSNorm's r (an fp32 reduction whose order is not fixed)
+Bars: INT8 codes, fp32 scales, INT32 accumulators and BF16 outputs
+bit-exact. The BF16 outputs may by the pages' tolerance differ by 1 BF16 ulp,
+but the kernels perform the oracle's fp32 operations in the oracle's order
+(post-scale: two RN products then one RN rounding to BF16; blockwise: one fma
+per K block in ascending order), so the results must be identical; the ulp
+distance is still logged. RMSNorm's r (an fp32 reduction whose order is not fixed)
 must be within (ceil(log2 K) + 4) * 2^-24 * r of the oracle's, and everything
 downstream of r is compared bit for bit given the device's r.
 """
@@ -284,11 +286,11 @@ def test_gemm_i32(shape, seed):
     assert np.array_equal(from_dev(out), ref)
 
 
-def ulp_report(got_bits, ref_bits, what):
+def exact_check(got_bits, ref_bits, what):
     d = O.bf16_ulp_distance(got_bits, ref_bits)
-    log(f"  {what}: max ulp {int(d.max()) if d.size else 0}, 1-ulp count {int(np.sum(d == 1))}"
+    log(f"  {what}: max ulp {int(d.max()) if d.size else 0}, differing {int(np.sum(d != 0))}"
         f" of {d.size}")
-    assert d.size == 0 or d.max() <= 1
+    assert np.array_equal(got_bits, ref_bits)
     return d
 
 
@@ -305,7 +307,7 @@ def test_gemm_postscale(shape, seed):
     out = w8.w8a8_gemm_postscale(to_dev(qa), to_dev(qw), to_dev(sa), to_dev(sw))
     sync()
     ref = O.postscale_bf16(O.gemm_i32(qa, qw), sa, sw)
-    ulp_report(bf16_from_dev(out), ref, "postscale vs oracle")
+    exact_check(bf16_from_dev(out), ref, "postscale vs oracle")
 
 
 BLOCKWISE_SHAPES = [((64, 128, 256), 61), ((1000, 5120, 5120), 62), ((300, 256, 384), 63),
@@ -328,7 +330,7 @@ def test_gemm_blockwise(shape, seed):
     out = w8.w8a8_gemm_blockwise(to_dev(qa), to_dev(qw), to_dev(sa), to_dev(sw))
     sync()
     ref = O.gemm_blockwise_bf16(qa, sa, qw, sw)
-    ulp_report(bf16_from_dev(out), ref, "blockwise vs oracle")
+    exact_check(bf16_from_dev(out), ref, "blockwise vs oracle")
 
 
 def test_gemm_blockwise_strides_and_guard():
@@ -347,7 +349,7 @@ def test_gemm_blockwise_strides_and_guard():
     w8.w8a8_gemm_blockwise(a_full[:, :K], w_full[:, :K], to_dev(sa), to_dev(sw), out=out)
     sync()
     ref = O.gemm_blockwise_bf16(qa, sa, qw, sw)
-    ulp_report(bf16_from_dev(out), ref, "strided blockwise vs oracle")
+    exact_check(bf16_from_dev(out), ref, "strided blockwise vs oracle")
     guard = bf16_from_dev(out_full)
     assert np.all(guard[M:] == 0xFFFF) and np.all(guard[:M, N:] == 0xFFFF)
 
@@ -392,7 +394,7 @@ def test_tiny_linear_end_to_end():
     sync()
     ref, qa_o, sa_o, qw_o, sw_o, acc = O.w8a8_linear(x, wb)
     assert np.array_equal(from_dev(qa), qa_o) and np.array_equal(from_dev(qw), qw_o)
-    ulp_report(bf16_from_dev(out), ref, "tiny linear")
+    exact_check(bf16_from_dev(out), ref, "tiny linear")
 
 
 def test_max_k_int32_extremes():

@@ -77,20 +77,20 @@ def test_splitk_strided_output_and_repeat():
         assert torch.all(full[:, N:] == -3.0)
 
 
-_FORCED_CHILD = r"""
-import sys
-import numpy as np, torch
-sys.path.insert(0, sys.argv[1])
-import oracle as O
-import workloads as W
-import w8a8_int8_quantized_token_amd as w8
-dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
-bad = 0
 # parts forced to 64, capped by the 128-byte K stages: one-stage parts, parts
 # of one or two stages, and as many parts as stages
-for (M, N, K, seed, want) in ((33, 128, 8192, 171, 64), (77, 384, 11136, 172, 64),
-                              (300, 768, 5248, 173, 41), (256, 512, 2048, 174, 16)):
-    assert w8.splitk_parts(M, N, K) == want, (M, N, K, w8.splitk_parts(M, N, K))
+FORCED = [((33, 128, 8192), 171, 64), ((77, 384, 11136), 172, 64),
+          ((300, 768, 5248), 173, 41), ((256, 512, 2048), 174, 16)]
+
+
+@pytest.mark.parametrize("shape,seed,parts", FORCED)
+def test_splitk_forced_parts_exact(shape, seed, parts):
+    """Many small parts, which the cost model does not pick: one-stage parts,
+    parts of unequal length, full-tile mode, with bias and GELU epilogues, the
+    part count passed explicitly and the workspace given by the caller."""
+    M, N, K = shape
+    log(f"split-K forced to {parts} parts: {shape}")
+    assert w8.postscale_workspace_size(M, N, K, parts) == parts * M * N * 4
     qa = W.random_int8((M, K), seed)
     qw = W.random_int8((N, K), seed + 1)
     qa[1] = 127
@@ -98,48 +98,47 @@ for (M, N, K, seed, want) in ((33, 128, 8192, 171, 64), (77, 384, 11136, 172, 64
     sa = W.random_scales((M,), seed + 2)
     sw = W.random_scales((N,), seed + 3, lo=1e-5, hi=1e-3)
     b = W.random_bits((N,), seed + 4, std=0.5)
+    ws = torch.empty((parts * M * N * 4,), dtype=torch.uint8, device="cuda")
+    acc = O.gemm_i32(qa, qw)
     for bias, gelu in ((None, False), (b, False), (b, True)):
-        out = w8.w8a8_gemm_postscale(dev(qa), dev(qw), dev(sa), dev(sw),
-                                     bias=None if bias is None else torch.from_numpy(np.ascontiguousarray(bias).view(np.int16)).view(torch.bfloat16).cuda(),
-                                     gelu=gelu)
+        out = w8.w8a8_gemm_postscale(to_dev(qa), to_dev(qw), to_dev(sa), to_dev(sw),
+                                     bias=None if bias is None else bf16_to_dev(bias),
+                                     gelu=gelu, parts=parts, workspace=ws)
         torch.cuda.synchronize()
-        got = out.view(torch.int16).cpu().numpy().view(np.uint16)
-        acc = O.gemm_i32(qa, qw)
         if gelu:
             ref = O.postscale_gelu_bf16(acc, sa, sw, bias)
         elif bias is None:
             ref = O.postscale_bf16(acc, sa, sw)
         else:
             ref = O.postscale_bias_bf16(acc, sa, sw, bias)
-        n = int(np.count_nonzero(got != ref))
-        print(f"{M}x{N}x{K} parts {want} bias={bias is not None} gelu={gelu}: {n} mismatches", flush=True)
-        bad += n
-sys.exit(0 if bad == 0 else 1)
-"""
+        got = bf16_from_dev(out)
+        log(f"  bias={bias is not None} gelu={gelu}: {int(np.count_nonzero(got != ref))} mismatches")
+        assert np.array_equal(got, ref)
 
 
-def test_splitk_forced_parts_exact():
-    """Many small parts (W8A8_SPLIT_K=64, capped by the K stages), which the cost
-    model no longer picks: one-stage parts, parts of unequal length, full-tile
-    mode, with bias and GELU epilogues; in a child process because the variable
-    is read once per process."""
-    import os
-    import subprocess
-    import sys
-    log("split-K with forced parts (child process)")
-    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    r = subprocess.run([sys.executable, "-c", _FORCED_CHILD, root], capture_output=True,
-                       text=True, timeout=240, env={**os.environ, "W8A8_SPLIT_K": "64"})
-    for line in r.stdout.strip().splitlines():
-        log("  " + line)
-    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+def test_splitk_workspace_rules_on_device():
+    """A workspace one byte short, or a forced split without one, is refused
+    before anything runs; the output keeps its contents."""
+    M, N, K = 64, 256, 1024
+    qa, qw = to_dev(W.random_int8((M, K), 175)), to_dev(W.random_int8((N, K), 176))
+    sa, sw = to_dev(W.random_scales((M,), 177)), to_dev(W.random_scales((N,), 178))
+    out = torch.full((M, N), 5.0, dtype=torch.bfloat16, device="cuda")
+    short = torch.empty((4 * M * N * 4 - 1,), dtype=torch.uint8, device="cuda")
+    with pytest.raises(w8.W8A8Error, match="workspace"):
+        w8.w8a8_gemm_postscale(qa, qw, sa, sw, out=out, parts=4, workspace=short)
+    st = w8.lib().w8a8_gemm_postscale_ex(qa.data_ptr(), K, qw.data_ptr(), K, sa.data_ptr(),
+                                         sw.data_ptr(), None, 0, out.data_ptr(), N, M, N, K, 4,
+                                         None, 0, torch.cuda.current_stream().cuda_stream)
+    assert st == w8.W8A8_ERR_INVALID_ARGUMENT and b"workspace" in w8.lib().w8a8_last_error()
+    torch.cuda.synchronize()
+    assert torch.all(out == 5.0)
 
 
 def test_concurrent_streams_exact():
     """Split-K and single-pass GEMMs issued on two side streams at once, many
-    times over: each split call takes its own stream-ordered workspace, so
-    concurrent calls never share partial sums. Every result is checked against
-    the oracle; the streams keep the default priority."""
+    times over: each split call gets its own workspace from torch's allocator
+    on its stream, so concurrent calls never share partial sums. Every result
+    is checked against the oracle; the streams keep the default priority."""
     log("concurrent split-K / single-pass GEMMs on two streams")
     cases = []
     for (M, N, K), seed in (((129, 5120, 13824), 181), ((64, 1024, 4096), 182),

@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "W8A8Error", "W8A8Unsupported", "lib", "LIB_PATH", "EXPORTED_SYMBOLS",
     "w8a8_quant_rows", "w8a8_rmsnorm_quant", "w8a8_layernorm_quant", "w8a8_gemm_postscale",
-    "w8a8_gemm_blockwise", "w8a8_gemm_i32", "w8a8_version", "Int8Linear",
+    "w8a8_gemm_blockwise", "w8a8_gemm_i32", "w8a8_version", "splitk_parts",
+    "postscale_workspace_size", "Int8Linear",
     "replace_linear_with_int8",
 ]
 
@@ -28,6 +29,7 @@ W8A8_ERR_INVALID_ARGUMENT = 1
 W8A8_ERR_UNSUPPORTED_SHAPE = 2
 W8A8_ERR_HIP = 3
 W8A8_MAX_K = 133120
+W8A8_EPILOGUE_GELU = 1
 
 
 class W8A8Error(RuntimeError):
@@ -61,6 +63,8 @@ _SIGS = {
     "w8a8_gemm_postscale_gelu": [_p, _i64, _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p],
     "w8a8_gemm_blockwise": [_p, _i64, _p, _i64, _p, _p, _p, _i64, _i64, _i64, _i64, _p],
     "w8a8_gemm_i32": [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p],
+    "w8a8_gemm_postscale_ex": [_p, _i64, _p, _i64, _p, _p, _p, ctypes.c_int32, _p, _i64, _i64,
+                               _i64, _i64, ctypes.c_int32, _p, _i64, _p],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -74,9 +78,11 @@ _lib.w8a8_version.argtypes = []
 _lib.w8a8_version.restype = ctypes.c_char_p
 _lib.w8a8_gemm_splitk_parts.argtypes = [_i64, _i64, _i64]
 _lib.w8a8_gemm_splitk_parts.restype = ctypes.c_int32
+_lib.w8a8_gemm_postscale_workspace_size.argtypes = [_i64, _i64, _i64, ctypes.c_int32]
+_lib.w8a8_gemm_postscale_workspace_size.restype = _i64
 
 EXPORTED_SYMBOLS = tuple(_SIGS) + ("w8a8_status_string", "w8a8_last_error", "w8a8_version",
-                                   "w8a8_gemm_splitk_parts")
+                                   "w8a8_gemm_splitk_parts", "w8a8_gemm_postscale_workspace_size")
 
 
 def lib() -> ctypes.CDLL:
@@ -112,26 +118,57 @@ def _ptr(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
 
 
-def _mat(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
-    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
-        raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, f"{name} must be a device tensor")
+# Buffer checks. The C ABI receives bare pointers and cannot see how large a
+# buffer is, so this layer checks every tensor's dtype, layout and size
+# against the call's shape (shape checks first, so that they are reported
+# even for tensors on the wrong device), then that all of them live on the
+# device the call runs on.
+
+def _bad(msg: str):
+    raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, msg)
+
+
+def _mat(t: torch.Tensor, dtype: torch.dtype, name: str, rows: int | None = None,
+         cols: int | None = None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        _bad(f"{name} must be a torch tensor")
     if t.dtype != dtype:
-        raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, f"{name} must be {dtype}, got {t.dtype}")
+        _bad(f"{name} must be {dtype}, got {t.dtype}")
     if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
-        raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, f"{name} must be a row-major 2-D matrix")
+        _bad(f"{name} must be a row-major 2-D matrix")
+    if (rows is not None and t.shape[0] != rows) or (cols is not None and t.shape[1] != cols):
+        _bad(f"{name} must have shape ({rows}, {cols}), got {tuple(t.shape)}")
     return t
 
 
 def _vec(t: torch.Tensor, dtype: torch.dtype, n: int, name: str) -> torch.Tensor:
-    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != dtype:
-        raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, f"{name} must be a {dtype} device tensor")
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype:
+        _bad(f"{name} must be a {dtype} tensor")
     if t.numel() != n or not t.is_contiguous():
-        raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, f"{name} must be contiguous with {n} elements")
+        _bad(f"{name} must be contiguous with {n} elements, got {tuple(t.shape)}")
     return t
+
+
+def _on_device(device: torch.device, **tensors) -> None:
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            _bad(f"{name} must be a device tensor")
+        if t.device != device:
+            _bad(f"{name} is on {t.device}, the call runs on {device}")
 
 
 def _ld(t: torch.Tensor) -> int:
     return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], t.stride(0))
+
+
+def _scale_elems(rows: int, cols: int, group_rows: int, group_cols: int) -> int | None:
+    """Scales a (group_rows, group_cols) quantisation of [rows, cols] writes, or
+    None for a group the library rejects anyway (nothing is launched then)."""
+    if group_rows <= 0 or group_cols <= 0 or cols % group_cols:
+        return None
+    return -(-rows // group_rows) * (cols // group_cols)
 
 
 def w8a8_quant_rows(x: torch.Tensor, group_rows: int = 1, group_cols: int | None = None,
@@ -147,11 +184,15 @@ def w8a8_quant_rows(x: torch.Tensor, group_rows: int = 1, group_cols: int | None
     gc = cols if group_cols is None else group_cols
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    n_sc = _scale_elems(rows, cols, group_rows, gc)
     if scale is None:
         n_gr = -(-rows // group_rows) if group_rows > 0 else 0
         shape = (n_gr,) if (group_rows == 1 and gc == cols) else (n_gr, cols // gc if gc > 0 else 0)
         scale = torch.empty(shape, dtype=torch.float32, device=x.device)
-    _mat(q, torch.int8, "q")
+    _mat(q, torch.int8, "q", rows, cols)
+    if n_sc is not None:
+        _vec(scale, torch.float32, n_sc, "scale")
+    _on_device(x.device, x=x, q=q, scale=scale)
     st = _lib.w8a8_quant_rows(_ptr(x), rows, cols, _ld(x), group_rows, gc, _ptr(q), _ld(q),
                               _ptr(scale), _stream(stream))
     _check(st, "w8a8_quant_rows")
@@ -174,7 +215,11 @@ def w8a8_rmsnorm_quant(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
         inv_rms = torch.empty((rows,), dtype=torch.float32, device=x.device)
     elif inv_rms is False:
         inv_rms = None
-    _mat(q, torch.int8, "q")
+    _mat(q, torch.int8, "q", rows, cols)
+    _vec(scale, torch.float32, rows, "scale")
+    if inv_rms is not None:
+        _vec(inv_rms, torch.float32, rows, "inv_rms")
+    _on_device(x.device, x=x, gamma=gamma, q=q, scale=scale, inv_rms=inv_rms)
     st = _lib.w8a8_rmsnorm_quant(_ptr(x), _ptr(gamma), float(eps), rows, cols, _ld(x), _ptr(q),
                                  _ld(q), _ptr(scale), _ptr(inv_rms), _stream(stream))
     _check(st, "w8a8_rmsnorm_quant")
@@ -208,7 +253,10 @@ def w8a8_layernorm_quant(x: torch.Tensor, eps: float = 1e-6, gamma: torch.Tensor
         _vec(rstd, torch.float32, rows, "rstd")
     else:
         mean = rstd = None
-    _mat(q, torch.int8, "q")
+    _mat(q, torch.int8, "q", rows, cols)
+    _vec(scale, torch.float32, rows, "scale")
+    _on_device(x.device, x=x, gamma=gamma, beta=beta, mod_scale=mod_scale, mod_shift=mod_shift,
+               q=q, scale=scale, mean=mean, rstd=rstd)
     st = _lib.w8a8_layernorm_quant(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(mod_scale),
                                    _ptr(mod_shift), float(eps), rows, cols, _ld(x), _ptr(q),
                                    _ld(q), _ptr(scale), _ptr(mean), _ptr(rstd), _stream(stream))
@@ -222,39 +270,55 @@ def _gemm_args(a, w, out, out_dtype):
     M, K = a.shape
     N, K2 = w.shape
     if K != K2:
-        raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, f"K mismatch: a has {K}, w has {K2}")
+        _bad(f"K mismatch: a has {K}, w has {K2}")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
-    _mat(out, out_dtype, "out")
+    _mat(out, out_dtype, "out", M, N)
     return M, N, K, out
+
+
+def postscale_workspace_size(M: int, N: int, K: int, parts: int = 0) -> int:
+    """Bytes of split-K workspace the post-scale GEMM needs for this shape with
+    `parts` (0 = the library's choice): 0 for a single pass, -1 if the library
+    would reject the arguments."""
+    return int(_lib.w8a8_gemm_postscale_workspace_size(M, N, K, parts))
 
 
 def w8a8_gemm_postscale(a: torch.Tensor, w: torch.Tensor, a_scale: torch.Tensor,
                         w_scale: torch.Tensor, out: torch.Tensor | None = None, stream=None,
-                        bias: torch.Tensor | None = None, gelu: bool = False):
+                        bias: torch.Tensor | None = None, gelu: bool = False, parts: int = 0,
+                        workspace: torch.Tensor | None = None):
     """out[M,N] (BF16) = bf16(acc * a_scale[m] * w_scale[n] (+ bias[n])), acc the
-    exact INT32 sum over K of a[m,k] * w[n,k]; with a bias this calls
-    w8a8_gemm_postscale_bias; with gelu=True, w8a8_gemm_postscale_gelu (GELU,
-    erf form, of that BF16 output)."""
+    exact INT32 sum over K of a[m,k] * w[n,k]; with gelu=True, the GELU (erf
+    form) of that BF16 output. Calls w8a8_gemm_postscale_ex: with parts=0 the
+    library chooses how many K parts to split into (few tokens, long K), 1 is
+    the single pass, n forces n parts. The split-K workspace is `workspace`
+    (a device tensor of at least the bytes postscale_workspace_size reports),
+    or one allocated here from torch's allocator on the call's stream."""
     M, N, K, out = _gemm_args(a, w, out, torch.bfloat16)
-    if gelu:
-        if bias is not None:
-            _vec(bias, torch.bfloat16, N, "bias")
-        st = _lib.w8a8_gemm_postscale_gelu(_ptr(a), _ld(a), _ptr(w), _ld(w), _ptr(a_scale),
-                                           _ptr(w_scale), None if bias is None else _ptr(bias),
-                                           _ptr(out), _ld(out), M, N, K, _stream(stream))
-        _check(st, "w8a8_gemm_postscale_gelu")
-        return out
-    if bias is None:
-        st = _lib.w8a8_gemm_postscale(_ptr(a), _ld(a), _ptr(w), _ld(w), _ptr(a_scale),
-                                      _ptr(w_scale), _ptr(out), _ld(out), M, N, K, _stream(stream))
-        _check(st, "w8a8_gemm_postscale")
-        return out
-    _vec(bias, torch.bfloat16, N, "bias")
-    st = _lib.w8a8_gemm_postscale_bias(_ptr(a), _ld(a), _ptr(w), _ld(w), _ptr(a_scale),
-                                       _ptr(w_scale), _ptr(bias), _ptr(out), _ld(out), M, N, K,
-                                       _stream(stream))
-    _check(st, "w8a8_gemm_postscale_bias")
+    _vec(a_scale, torch.float32, M, "a_scale")
+    _vec(w_scale, torch.float32, N, "w_scale")
+    if bias is not None:
+        _vec(bias, torch.bfloat16, N, "bias")
+    _on_device(a.device, a=a, w=w, out=out, a_scale=a_scale, w_scale=w_scale, bias=bias,
+               workspace=workspace)
+    need = postscale_workspace_size(M, N, K, parts) if M > 0 else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=a.device)
+        if stream is not None:
+            # the allocator may hand this block out again once `stream`'s work
+            # that uses it is done, not merely the current stream's
+            sobj = stream if isinstance(stream, torch.cuda.Stream) else \
+                torch.cuda.ExternalStream(int(stream), device=a.device)
+            workspace.record_stream(sobj)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is not None and not workspace.is_contiguous():
+        _bad("workspace must be contiguous")
+    st = _lib.w8a8_gemm_postscale_ex(_ptr(a), _ld(a), _ptr(w), _ld(w), _ptr(a_scale),
+                                     _ptr(w_scale), _ptr(bias), W8A8_EPILOGUE_GELU if gelu else 0,
+                                     _ptr(out), _ld(out), M, N, K, int(parts), _ptr(workspace),
+                                     ws_bytes, _stream(stream))
+    _check(st, "w8a8_gemm_postscale_ex")
     return out
 
 
@@ -262,6 +326,10 @@ def w8a8_gemm_blockwise(a: torch.Tensor, w: torch.Tensor, a_scale: torch.Tensor,
                         w_scale: torch.Tensor, out: torch.Tensor | None = None, stream=None):
     """Blockwise-scaled GEMM: a_scale [M, K/128], w_scale [N/128, K/128]."""
     M, N, K, out = _gemm_args(a, w, out, torch.bfloat16)
+    if K % 128 == 0 and N % 128 == 0:         # other shapes: the library rejects them
+        _vec(a_scale, torch.float32, M * (K // 128), "a_scale")
+        _vec(w_scale, torch.float32, (N // 128) * (K // 128), "w_scale")
+    _on_device(a.device, a=a, w=w, out=out, a_scale=a_scale, w_scale=w_scale)
     st = _lib.w8a8_gemm_blockwise(_ptr(a), _ld(a), _ptr(w), _ld(w), _ptr(a_scale), _ptr(w_scale),
                                   _ptr(out), _ld(out), M, N, K, _stream(stream))
     _check(st, "w8a8_gemm_blockwise")
@@ -271,6 +339,7 @@ def w8a8_gemm_blockwise(a: torch.Tensor, w: torch.Tensor, a_scale: torch.Tensor,
 def w8a8_gemm_i32(a: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = None, stream=None):
     """The post-scale GEMM's INT32 accumulators, out[m,n] = sum_k a[m,k] * w[n,k]."""
     M, N, K, out = _gemm_args(a, w, out, torch.int32)
+    _on_device(a.device, a=a, w=w, out=out)
     st = _lib.w8a8_gemm_i32(_ptr(a), _ld(a), _ptr(w), _ld(w), _ptr(out), _ld(out), M, N, K,
                             _stream(stream))
     _check(st, "w8a8_gemm_i32")

@@ -93,6 +93,69 @@ w8a8_status_t check_gemm_common(const int8_t* a, int64_t lda, const int8_t* w, i
   return W8A8_OK;
 }
 
+// Parts a post-scale call runs with: `parts` == 0 asks for the library's
+// choice (the split-K cost model), else exactly `parts`. Returns -1 if
+// `parts` is out of range for K.
+int resolve_parts(int64_t M, int64_t N, int64_t K, int32_t parts) {
+  if (parts < 0 || parts > w8a8::kMaxSplitParts || parts > K / 128) return -1;
+  if (parts > 0) return parts;
+  if (M <= 0) return 1;
+  return w8a8::splitk_parts(M, N, K, w8a8::device_cu_count());
+}
+
+// The whole post-scale family: validation, then the single pass or split-K
+// into the caller's workspace.
+w8a8_status_t postscale_call(const char* name, const int8_t* a, int64_t lda, const int8_t* w,
+                             int64_t ldw, const float* a_scale, const float* w_scale,
+                             const uint16_t* bias, bool gelu, uint16_t* out, int64_t ldo,
+                             int64_t M, int64_t N, int64_t K, int32_t parts, void* workspace,
+                             int64_t workspace_bytes, void* stream) {
+  w8a8_status_t st = check_gemm_common(a, lda, w, ldw, out, ldo, 2, M, N, K);
+  if (st != W8A8_OK) return st;
+  const int resolved = resolve_parts(M, N, K, parts);
+  if (resolved < 0)
+    return fail(W8A8_ERR_INVALID_ARGUMENT, "parts must be 0 (library's choice) or 1..%d and at most K/128",
+                w8a8::kMaxSplitParts);
+  if (workspace_bytes < 0) return fail(W8A8_ERR_INVALID_ARGUMENT, "negative workspace_bytes");
+  if (M == 0) return ok();
+  if (!a_scale || !w_scale) return fail(W8A8_ERR_INVALID_ARGUMENT, "null scale pointer");
+  if (!aligned(a_scale, 4) || !aligned(w_scale, 4)) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "scales must be 4-byte aligned");
+  if (bias && !aligned(bias, 16)) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "bias must be 16-byte aligned");
+  const size_t ob = span_bytes(M, N, ldo, 2);
+  if (overlap(out, ob, a_scale, (size_t)M * 4) || overlap(out, ob, w_scale, (size_t)N * 4) ||
+      (bias && overlap(out, ob, bias, (size_t)N * 2)))
+    return fail(W8A8_ERR_INVALID_ARGUMENT, "output overlaps a scale or the bias");
+  int run_parts = resolved;
+  if (resolved > 1) {
+    if (M * N > ((int64_t)1 << 50)) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "M * N too large to split");
+    const int64_t need = (int64_t)resolved * M * N * 4;
+    if (!workspace) {
+      // the library's own choice falls back to the single pass; parts the
+      // caller asked for need the workspace
+      if (parts > 1)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "%d parts need a workspace of %lld bytes",
+                    resolved, (long long)need);
+      run_parts = 1;
+    } else {
+      if (workspace_bytes < need)
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "workspace of %lld bytes, %d parts need %lld",
+                    (long long)workspace_bytes, resolved, (long long)need);
+      if (!aligned(workspace, 16)) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "workspace must be 16-byte aligned");
+      const size_t wb = (size_t)need;
+      if (overlap(workspace, wb, out, ob) || overlap(workspace, wb, a, span_bytes(M, K, lda, 1)) ||
+          overlap(workspace, wb, w, span_bytes(N, K, ldw, 1)) ||
+          overlap(workspace, wb, a_scale, (size_t)M * 4) || overlap(workspace, wb, w_scale, (size_t)N * 4) ||
+          (bias && overlap(workspace, wb, bias, (size_t)N * 2)))
+        return fail(W8A8_ERR_INVALID_ARGUMENT, "workspace overlaps an input or the output");
+    }
+  }
+  const w8a8::Epilogue epi = bias ? (gelu ? w8a8::Epilogue::kPostscaleBiasGeluBf16 : w8a8::Epilogue::kPostscaleBiasBf16)
+                                  : (gelu ? w8a8::Epilogue::kPostscaleGeluBf16 : w8a8::Epilogue::kPostscaleBf16);
+  return from_hip(w8a8::launch_gemm(epi, a, lda, w, ldw, a_scale, w_scale, bias, out, ldo, M, N, K,
+                                    (hipStream_t)stream, run_parts, workspace),
+                  name);
+}
+
 }  // namespace
 
 extern "C" {
@@ -207,58 +270,48 @@ w8a8_status_t w8a8_layernorm_quant(const uint16_t* x, const uint16_t* gamma,
 w8a8_status_t w8a8_gemm_postscale(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
                                   const float* a_scale, const float* w_scale, uint16_t* out,
                                   int64_t ldo, int64_t M, int64_t N, int64_t K, void* stream) {
-  w8a8_status_t st = check_gemm_common(a, lda, w, ldw, out, ldo, 2, M, N, K);
-  if (st != W8A8_OK) return st;
-  if (M == 0) return ok();
-  if (!a_scale || !w_scale) return fail(W8A8_ERR_INVALID_ARGUMENT, "null scale pointer");
-  if (!aligned(a_scale, 4) || !aligned(w_scale, 4)) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "scales must be 4-byte aligned");
-  const size_t ob = span_bytes(M, N, ldo, 2);
-  if (overlap(out, ob, a_scale, (size_t)M * 4) || overlap(out, ob, w_scale, (size_t)N * 4))
-    return fail(W8A8_ERR_INVALID_ARGUMENT, "output overlaps a scale");
-  if (M == 0) return ok();
-  return from_hip(w8a8::launch_gemm(w8a8::Epilogue::kPostscaleBf16, a, lda, w, ldw, a_scale, w_scale, nullptr,
-                                    out, ldo, M, N, K, (hipStream_t)stream),
-                  "w8a8_gemm_postscale launch");
+  return postscale_call("w8a8_gemm_postscale launch", a, lda, w, ldw, a_scale, w_scale, nullptr,
+                        false, out, ldo, M, N, K, 1, nullptr, 0, stream);
 }
 
 w8a8_status_t w8a8_gemm_postscale_bias(const int8_t* a, int64_t lda, const int8_t* w,
                                        int64_t ldw, const float* a_scale, const float* w_scale,
                                        const uint16_t* bias, uint16_t* out, int64_t ldo,
                                        int64_t M, int64_t N, int64_t K, void* stream) {
-  w8a8_status_t st = check_gemm_common(a, lda, w, ldw, out, ldo, 2, M, N, K);
-  if (st != W8A8_OK) return st;
-  if (M == 0) return ok();
-  if (!a_scale || !w_scale || !bias) return fail(W8A8_ERR_INVALID_ARGUMENT, "null scale or bias pointer");
-  if (!aligned(a_scale, 4) || !aligned(w_scale, 4)) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "scales must be 4-byte aligned");
-  if (!aligned(bias, 16)) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "bias must be 16-byte aligned");
-  const size_t ob = span_bytes(M, N, ldo, 2);
-  if (overlap(out, ob, a_scale, (size_t)M * 4) || overlap(out, ob, w_scale, (size_t)N * 4) ||
-      overlap(out, ob, bias, (size_t)N * 2))
-    return fail(W8A8_ERR_INVALID_ARGUMENT, "output overlaps a scale or the bias");
-  return from_hip(w8a8::launch_gemm(w8a8::Epilogue::kPostscaleBiasBf16, a, lda, w, ldw, a_scale,
-                                    w_scale, bias, out, ldo, M, N, K, (hipStream_t)stream),
-                  "w8a8_gemm_postscale_bias launch");
+  if (M > 0 && !bias) {
+    w8a8_status_t st = check_gemm_common(a, lda, w, ldw, out, ldo, 2, M, N, K);
+    return st != W8A8_OK ? st : fail(W8A8_ERR_INVALID_ARGUMENT, "null bias pointer");
+  }
+  return postscale_call("w8a8_gemm_postscale_bias launch", a, lda, w, ldw, a_scale, w_scale, bias,
+                        false, out, ldo, M, N, K, 1, nullptr, 0, stream);
 }
 
 w8a8_status_t w8a8_gemm_postscale_gelu(const int8_t* a, int64_t lda, const int8_t* w,
                                        int64_t ldw, const float* a_scale, const float* w_scale,
                                        const uint16_t* bias, uint16_t* out, int64_t ldo,
                                        int64_t M, int64_t N, int64_t K, void* stream) {
-  w8a8_status_t st = check_gemm_common(a, lda, w, ldw, out, ldo, 2, M, N, K);
-  if (st != W8A8_OK) return st;
-  if (M == 0) return ok();
-  if (!a_scale || !w_scale) return fail(W8A8_ERR_INVALID_ARGUMENT, "null scale pointer");
-  if (!aligned(a_scale, 4) || !aligned(w_scale, 4)) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "scales must be 4-byte aligned");
-  if (bias && !aligned(bias, 16)) return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "bias must be 16-byte aligned");
-  const size_t ob = span_bytes(M, N, ldo, 2);
-  if (overlap(out, ob, a_scale, (size_t)M * 4) || overlap(out, ob, w_scale, (size_t)N * 4) ||
-      (bias && overlap(out, ob, bias, (size_t)N * 2)))
-    return fail(W8A8_ERR_INVALID_ARGUMENT, "output overlaps a scale or the bias");
-  return from_hip(w8a8::launch_gemm(bias ? w8a8::Epilogue::kPostscaleBiasGeluBf16
-                                         : w8a8::Epilogue::kPostscaleGeluBf16,
-                                    a, lda, w, ldw, a_scale, w_scale, bias, out, ldo, M, N, K,
-                                    (hipStream_t)stream),
-                  "w8a8_gemm_postscale_gelu launch");
+  return postscale_call("w8a8_gemm_postscale_gelu launch", a, lda, w, ldw, a_scale, w_scale, bias,
+                        true, out, ldo, M, N, K, 1, nullptr, 0, stream);
+}
+
+w8a8_status_t w8a8_gemm_postscale_ex(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
+                                     const float* a_scale, const float* w_scale,
+                                     const uint16_t* bias, int32_t flags, uint16_t* out,
+                                     int64_t ldo, int64_t M, int64_t N, int64_t K, int32_t parts,
+                                     void* workspace, int64_t workspace_bytes, void* stream) {
+  if (flags & ~W8A8_EPILOGUE_GELU) return fail(W8A8_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", (unsigned)flags);
+  return postscale_call("w8a8_gemm_postscale_ex launch", a, lda, w, ldw, a_scale, w_scale, bias,
+                        (flags & W8A8_EPILOGUE_GELU) != 0, out, ldo, M, N, K, parts, workspace,
+                        workspace_bytes, stream);
+}
+
+int64_t w8a8_gemm_postscale_workspace_size(int64_t M, int64_t N, int64_t K, int32_t parts) {
+  if (M < 0 || N < 128 || N % 128 || K < 128 || K % 128 || K > W8A8_MAX_K || M > kMaxRows ||
+      N > kMaxRows)
+    return -1;
+  const int resolved = resolve_parts(M, N, K, parts);
+  if (resolved < 0 || (resolved > 1 && M * N > ((int64_t)1 << 50))) return -1;
+  return resolved > 1 ? (int64_t)resolved * M * N * 4 : 0;
 }
 
 w8a8_status_t w8a8_gemm_blockwise(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,

@@ -12,32 +12,26 @@ namespace w8a8 {
 
 hipError_t launch_gemm(Epilogue epi, const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
                        const float* a_scale, const float* w_scale, const uint16_t* bias,
-                       void* out, int64_t ldo, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+                       void* out, int64_t ldo, int64_t M, int64_t N, int64_t K, hipStream_t st,
+                       int parts, void* ws) {
   if (M == 0) return hipSuccess;
   switch (epi) {
     case Epilogue::kPostscaleBf16:
     case Epilogue::kPostscaleBiasBf16:
     case Epilogue::kPostscaleGeluBf16:
     case Epilogue::kPostscaleBiasGeluBf16: {
-      // Too few tiles to fill the chip: K in parts, INT32 partial sums in a
-      // stream-ordered workspace, then one pass that adds them and applies
-      // the epilogue (bit-identical to the single pass). If the workspace
-      // cannot be had, the single pass runs instead.
-      const int parts = splitk_parts(M, N, K, device_cu_count());
+      // K in parts: exact INT32 partial sums in the caller's workspace, then
+      // one pass that adds them and applies the epilogue (bit-identical to
+      // the single pass).
       if (parts > 1) {
-        void* ws = nullptr;
-        if (hipMallocAsync(&ws, (size_t)parts * M * N * 4, st) == hipSuccess) {
-          hipError_t e = launch_gemm_pipelined(Epilogue::kInt32, a, lda, w, ldw, nullptr, nullptr,
-                                               nullptr, ws, N, M, N, K, st, parts);
-          if (e == hipSuccess)
-            e = launch_splitk_postscale(
-                static_cast<const int32_t*>(ws), parts, M, N, a_scale, w_scale,
-                epilogue_has_bias(epi) ? bias : nullptr, epilogue_has_gelu(epi),
-                reinterpret_cast<uint16_t*>(out), ldo, st);
-          const hipError_t f = hipFreeAsync(ws, st);
-          return e != hipSuccess ? e : f;
-        }
-        (void)hipGetLastError();   // the failed allocation is not the caller's error
+        if (!ws) return hipErrorInvalidValue;
+        hipError_t e = launch_gemm_pipelined(Epilogue::kInt32, a, lda, w, ldw, nullptr, nullptr,
+                                             nullptr, ws, N, M, N, K, st, parts);
+        if (e != hipSuccess) return e;
+        return launch_splitk_postscale(static_cast<const int32_t*>(ws), parts, M, N, a_scale,
+                                       w_scale, epilogue_has_bias(epi) ? bias : nullptr,
+                                       epilogue_has_gelu(epi), reinterpret_cast<uint16_t*>(out),
+                                       ldo, st);
       }
       return launch_gemm_pipelined(epi, a, lda, w, ldw, a_scale, w_scale, bias, out, ldo, M, N, K,
                                    st);

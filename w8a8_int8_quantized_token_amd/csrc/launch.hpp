@@ -63,11 +63,15 @@ hipError_t launch_splitk_postscale(const int32_t* ws, int splits, int64_t M, int
                                    const uint16_t* bias, bool gelu, uint16_t* out, int64_t ldo,
                                    hipStream_t st);
 
+// Split-K limits: at most this many K parts, and the library's own choice
+// never asks for a larger workspace than this (bytes).
+constexpr int kMaxSplitParts = 64;
+constexpr int64_t kMaxSplitWorkspace = (int64_t)1 << 30;
+
 // K parts for a post-scale GEMM of this shape on `cus` compute units, from a
 // cost model of the split (fewer stages per work item against a per-item
 // cost, the partial sums' traffic, a fixed cost and the host's floor); 1
-// unless splitting saves 15% of the time. The W8A8_SPLIT_K environment
-// variable overrides it (1 disables splitting).
+// unless splitting saves 15% of the time. A pure function of its arguments.
 int splitk_parts(int64_t M, int64_t N, int64_t K, int cus);
 
 // Persistent pipelined kernel with per-K-block scales.
@@ -75,9 +79,13 @@ hipError_t launch_gemm_blockwise(const int8_t* a, int64_t lda, const int8_t* w, 
                                  const float* a_scale, const float* w_scale, uint16_t* out,
                                  int64_t ldo, int64_t M, int64_t N, int64_t K, hipStream_t st);
 
-// bias (BF16 [N]) is read by the kPostscaleBiasBf16 epilogue only.
+// bias (BF16 [N]) is read by the bias epilogues only. A post-scale epilogue
+// with parts > 1 runs split-K: the INT32 partial sums of the parts go to the
+// caller's workspace ws (parts * M * N int32, 16-byte aligned), then one pass
+// adds them and applies the epilogue; parts == 1 is the single pass.
 hipError_t launch_gemm(Epilogue epi, const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
                        const float* a_scale, const float* w_scale, const uint16_t* bias,
-                       void* out, int64_t ldo, int64_t M, int64_t N, int64_t K, hipStream_t st);
+                       void* out, int64_t ldo, int64_t M, int64_t N, int64_t K, hipStream_t st,
+                       int parts = 1, void* ws = nullptr);
 
 }  // namespace w8a8

@@ -10,8 +10,6 @@
 //
 // One thread per 8 consecutive outputs of a row: per part two 16-byte loads,
 // one 16-byte store. The partial sums are read once (non-temporal).
-#include <cstdlib>
-
 #include "launch.hpp"
 #include "pipeline.hpp"
 
@@ -93,17 +91,7 @@ hipError_t launch_splitk_postscale(const int32_t* ws, int splits, int64_t M, int
 
 int splitk_parts(int64_t M, int64_t N, int64_t K, int cus) {
   const int64_t nk = K / 128;
-  static const int forced = [] {
-    const char* e = std::getenv("W8A8_SPLIT_K");
-    return e ? std::atoi(e) : 0;
-  }();
   const int64_t bytes_per_part = M * N * 4;
-  constexpr int64_t kMaxWorkspace = (int64_t)1 << 30;
-  if (forced > 0) {
-    int64_t parts = forced < nk ? forced : nk;
-    while (parts > 1 && parts * bytes_per_part > kMaxWorkspace) --parts;
-    return (int)parts;
-  }
   // Cost model in microseconds, fitted to timings of split and single passes
   // on MI355X (M from 64 to 2048, N from 1024 to 16384, K from 4096 to 13824,
   // 1 to 24 parts):
@@ -112,19 +100,19 @@ int splitk_parts(int64_t M, int64_t N, int64_t K, int cus) {
   //  * split: per round of work items, 1.3 per stage plus 3 for the item's
   //    prologue and INT32 epilogue; 11 for the extra pass and the workspace;
   //    0.286 per MB of partial sums (written once, read once); and never
-  //    below 25, what the host needs to issue the allocation, two launches
-  //    and the release.
+  //    below 25 (the fit's floor, measured when each split call also took
+  //    and released its workspace on the stream).
   // Split only if that saves 15%, and then take the fewest parts within 5%
   // of the best (fewer partial bytes, same predicted time).
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
   const double stage_us = 1.3, item_us = 3.0, fixed_us = 11.0, us_per_byte = 0.286e-6,
                floor_us = 25.0;
   const double single = (double)((tiles + cus - 1) / cus) * nk * stage_us;
-  double est[65] = {0};
+  double est[kMaxSplitParts + 1] = {0};
   double best_us = 0.0;
   int64_t last = 1;
-  for (int64_t parts = 2; parts <= nk && parts <= 64; ++parts) {
-    if (parts * bytes_per_part > kMaxWorkspace) break;
+  for (int64_t parts = 2; parts <= nk && parts <= kMaxSplitParts; ++parts) {
+    if (parts * bytes_per_part > kMaxSplitWorkspace) break;
     const double rounds = (double)((tiles * parts + cus - 1) / cus);
     double us = rounds * ((double)((nk + parts - 1) / parts) * stage_us + item_us) + fixed_us +
                 us_per_byte * (double)(parts * bytes_per_part);
