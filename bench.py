@@ -48,6 +48,9 @@ def parse():
     # needs ~150 ms of load to ramp before timing is representative
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="up_proj")
+    p.add_argument("--preload-ms", type=float, default=250.0,
+                   help="untimed load before the timed steps: at least this much wall time "
+                        "(and at least --warmup steps)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-bf16", action="store_true", help="skip the torch BF16 Linear yardstick")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -153,6 +156,59 @@ def measure_mainloop_ceiling(verbose: bool = False):
     return {"workgroups": grid, "stages": stages, "results": results}
 
 
+class ClockStamps:
+    """Average shader clock over a region of one stream's work, from the probe
+    library's stamp kernel (one workgroup per CU records its CU id, the shader
+    clock counter and the 100 MHz real-time counter) launched before and after
+    the region. None when the probe library is not built."""
+
+    def __init__(self, stream):
+        import ctypes
+        import torch
+        path = os.path.join(ROOT, "w8a8_int8_quantized_token_amd", "libw8a8_probe.so")
+        self.ok = os.path.exists(path)
+        if not self.ok:
+            return
+        self.lib = ctypes.CDLL(path)
+        self.lib.w8a8_probe_clock_stamp.restype = ctypes.c_int
+        self.lib.w8a8_probe_clock_stamp.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                                    ctypes.c_void_p]
+        self.lib.w8a8_probe_mainloop_workgroups.restype = ctypes.c_int
+        self.wg = max(1, self.lib.w8a8_probe_mainloop_workgroups())
+        self.buf = [torch.zeros(4 * self.wg, dtype=torch.int64, device="cuda") for _ in range(2)]
+        self.stream = stream
+
+    def stamp(self, which: int) -> None:
+        if self.ok:
+            b = self.buf[which]
+            rc = self.lib.w8a8_probe_clock_stamp(b.data_ptr(), b.numel(), self.wg,
+                                                 self.stream.cuda_stream)
+            if rc != 0:
+                self.ok = False
+
+    def ghz(self):
+        """Mean over CUs of (shader cycles / real time) between the stamps."""
+        if not self.ok:
+            return None
+        a = self.buf[0].view(-1, 4).cpu().numpy()
+        b = self.buf[1].view(-1, 4).cpu().numpy()
+        first_a, first_b = {}, {}
+        for rec, d in ((a, first_a), (b, first_b)):
+            for key, t, r, _ in rec:
+                d.setdefault(int(key), (int(t), int(r)))
+        rates = []
+        for key, (t0, r0) in first_a.items():
+            if key in first_b:
+                t1, r1 = first_b[key]
+                if r1 > r0 and t1 > t0:
+                    rates.append((t1 - t0) / ((r1 - r0) * 10.0))      # cycles per ns = GHz
+        if not rates:
+            return None
+        return {"ghz_mean": round(float(np.mean(rates)), 4),
+                "ghz_min": round(float(np.min(rates)), 4),
+                "ghz_max": round(float(np.max(rates)), 4), "cus": len(rates)}
+
+
 def mainloop_ceiling() -> None:
     res = measure_mainloop_ceiling(verbose=True)
     if res is None:
@@ -181,6 +237,21 @@ def load_traffic(kernel: str, workload: str, src_hash: str):
     if rec.get("source_hash") != src_hash:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def load_counters(kernel: str, workload: str, src_hash: str):
+    """MFMA and clock counters of one launch from a committed rocprofv3 --pmc
+    summary (profiles/mfma_<kernel>_<workload>.json), or None if there is none
+    or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"mfma_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != src_hash:
+        return None
+    return {k: rec[k] for k in ("mfma_busy_frac", "clock_ghz", "frac_of_peak_at_clock",
+                                "mfma_ops_counted", "source") if k in rec}
 
 
 def main():
@@ -287,14 +358,26 @@ def main():
             w8.w8a8_gemm_postscale(qa, qw, sa, sw, out=out, bias=bias, gelu=wl.gelu)
 
     ops = 2 * M * N * K
-    for i in range(args.warmup):
-        quant(xs[i % N_ROTATE])
-        gemm()
-    torch.cuda.synchronize()
+    # Untimed load: the --warmup steps, then more steps until at least
+    # PRELOAD_MS of wall time has passed (the engine clock ramps over
+    # ~150 ms of load; a step count alone can leave it short of steady state).
+    t_pre = time.perf_counter()
+    done = 0
+    while True:
+        for _ in range(5):
+            quant(xs[done % N_ROTATE])
+            gemm()
+            done += 1
+        torch.cuda.synchronize()
+        if done >= args.warmup and (time.perf_counter() - t_pre) * 1e3 >= args.preload_ms:
+            break
+    preload_ms = (time.perf_counter() - t_pre) * 1e3
 
+    clock = ClockStamps(stream)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    clock.stamp(0)
     for i in range(args.steps):
         e = evs[i]
         e[0].record(stream)
@@ -302,12 +385,25 @@ def main():
         e[1].record(stream)
         gemm()
         e[2].record(stream)
+    clock.stamp(1)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_start
     quant_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     gemm_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
     ms_per_step = wall_s * 1e3 / args.steps
+
+    # The quant kernel alone, back to back over the rotated inputs between one
+    # event pair: its sustained rate, without the per-launch event gaps that
+    # the per-step pairs add to a ~60 us kernel.
+    q_reps = 30
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(q_reps):
+        quant(xs[i % N_ROTATE])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    quant_b2b_ms = e0.elapsed_time(e1) / q_reps
 
     gemm_avg = float(gemm_ms.mean())
     gemm_tops = ops / (gemm_avg * 1e-3) / 1e12
@@ -321,11 +417,25 @@ def main():
     extra = {
         "gemm_ms_avg": round(gemm_avg, 4), "gemm_ms_min": round(float(gemm_ms.min()), 4),
         "gemm_tops": round(gemm_tops, 1), "gemm_frac_int8_peak": round(gemm_tops / INT8_PEAK_TOPS, 4),
-        f"{quant_name}_ms_avg": round(quant_avg, 4), f"{quant_name}_gbs": round(quant_gbs, 1),
-        f"{quant_name}_frac_hbm_peak": round(quant_gbs / HBM_PEAK_GBS, 4),
+        f"{quant_name}_ms_avg": round(quant_b2b_ms, 4),
+        f"{quant_name}_gbs": round(quant_bytes / (quant_b2b_ms * 1e-3) / 1e9, 1),
+        f"{quant_name}_frac_hbm_peak": round(quant_bytes / (quant_b2b_ms * 1e-3) / 1e9
+                                             / HBM_PEAK_GBS, 4),
+        f"{quant_name}_ms_in_step": round(quant_avg, 4), f"{quant_name}_gbs_in_step": round(quant_gbs, 1),
         "event_step_ms_avg": round(float(step_ms.mean()), 4),
         "weight_quant_ms": round(wquant_ms, 4), "input_gen_s": round(gen_s, 1),
+        "preload_ms": round(preload_ms, 1), "preload_steps": done,
     }
+    clk = clock.ghz()
+    if clk is not None:
+        # the shader clock over the timed region, and the GEMM's rate over the
+        # peak at that clock (the share of cycles its MFMAs were busy)
+        extra["shader_clock_timed_region"] = clk
+        extra["gemm_frac_of_peak_at_measured_clock"] = round(
+            gemm_tops / (INT8_PEAK_TOPS * clk["ghz_mean"] / 2.4), 4)
+    mfma = load_counters(gemm_name, args.workload, source_hash(*GEMM_SOURCES))
+    if mfma is not None:
+        extra["gemm_counters"] = mfma
 
     # ---- the pages' yardstick: torch's BF16 Linear on the same shape ---------
     if not args.no_bf16:
@@ -390,26 +500,54 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(wl, x_host, w_host, budget_s):
-    """The oracle, as it stands, on as many leading rows as fit the time budget."""
-    import oracle as O
+def cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, x_host, w_host, budget_s):
+    """The oracle, as it stands, on as many leading token rows as fit the time
+    budget, on every core of this process's affinity mask: the row chunk's
+    quantisation (and norm) runs as one oracle call per sub-chunk on a thread
+    pool (numpy releases the GIL), the GEMM and epilogue as one oracle call on
+    the chunk with BLAS threads set to the same count."""
+    import concurrent.futures as cf
+    import oracle as O
+    import workloads as W
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
     except Exception:  # pragma: no cover
-        cores = 1
+        limiter = None
+    pool = cf.ThreadPoolExecutor(max_workers=cores)
     t0 = time.perf_counter()
     if wl.blockwise:
         qw, sw = O.quantize_groups(w_host, 128, 128)
     else:
         qw, sw = O.quantize_rows(w_host)
     t_w = time.perf_counter() - t0
-    rows_done = 0
-    chunk = 256
-    t_path = 0.0
-    g = None
-    import workloads as W
     b = W.bias_bits(wl) if wl.bias_std > 0 else None
+    g = W.gamma_bits(wl) if wl.norm else None
+    msc = W.mod_bits(wl, "mod_scale") if wl.layernorm else None
+    msh = W.mod_bits(wl, "mod_shift") if wl.layernorm else None
+
+    def quant_part(x):
+        if wl.norm:
+            qa, sa, _ = O.rmsnorm_quant(x, g, wl.eps)
+        elif wl.layernorm:
+            qa, sa, _, _ = O.layernorm_quant(x, wl.eps, scale_bits=msc, shift_bits=msh)
+        elif wl.blockwise:
+            qa, sa = O.quantize_groups(x, 1, 128)
+        else:
+            qa, sa = O.quantize_rows(x)
+        return qa, sa
 
     def epilogue(acc, sa):
         if wl.gelu:
@@ -417,32 +555,32 @@ def cpu_baseline(wl, x_host, w_host, budget_s):
         if b is not None:
             return O.postscale_bias_bf16(acc, sa, sw, b)
         return O.postscale_bf16(acc, sa, sw)
-    if wl.norm or wl.layernorm:
-        g = W.gamma_bits(wl) if wl.norm else None
-        msc = W.mod_bits(wl, "mod_scale") if wl.layernorm else None
-        msh = W.mod_bits(wl, "mod_shift") if wl.layernorm else None
-    while rows_done < wl.M and t_path < budget_s:
-        r1 = min(rows_done + chunk, wl.M)
+
+    rows_done = 0
+    chunk = 256
+    t_path = 0.0
+    n_rows = min(wl.M, x_host.shape[0])
+    while rows_done < n_rows and t_path < budget_s:
+        r1 = min(rows_done + chunk, n_rows)
         x = x_host[rows_done:r1]
         t1 = time.perf_counter()
-        if wl.norm:
-            qa, sa, _ = O.rmsnorm_quant(x, g, wl.eps)
-            epilogue(O.gemm_i32(qa, qw), sa)
-        elif wl.layernorm:
-            qa, sa, _, _ = O.layernorm_quant(x, wl.eps, scale_bits=msc, shift_bits=msh)
-            epilogue(O.gemm_i32(qa, qw), sa)
-        elif wl.blockwise:
-            qa, sa = O.quantize_groups(x, 1, 128)
+        bounds = np.linspace(0, x.shape[0], min(cores, max(1, x.shape[0] // 16)) + 1).astype(int)
+        res = list(pool.map(lambda ab: quant_part(x[ab[0]:ab[1]]), zip(bounds[:-1], bounds[1:])))
+        qa = np.concatenate([r[0] for r in res])
+        sa = np.concatenate([r[1] for r in res])
+        if wl.blockwise:
             O.gemm_blockwise_bf16(qa, sa, qw, sw)
         else:
-            qa, sa = O.quantize_rows(x)
             epilogue(O.gemm_i32(qa, qw), sa)
         t_path += time.perf_counter() - t1
         rows_done = r1
         chunk = min(chunk * 2, 4096)
+    pool.shutdown()
+    if limiter is not None and hasattr(limiter, "restore_original_limits"):
+        limiter.restore_original_limits()
     ops = 2 * rows_done * wl.N * wl.K
     return {"value": round(ops / t_path / 1e12, 5), "unit": "TOP/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"first {rows_done} of {wl.M} token rows through the whole per-call path "
                       f"({t_path:.1f} s); weight quant of all {wl.N} rows took {t_w:.1f} s, excluded"}
 
