@@ -275,6 +275,31 @@ w8a8_status_t w8a8_gemm_postscale_ex(const int8_t* a, int64_t lda, const int8_t*
 int64_t w8a8_gemm_postscale_workspace_size(int64_t M, int64_t N, int64_t K, int32_t parts);
 
 /*
+ * w8a8_gemm_postscale_noalloc -- w8a8_gemm_postscale_ex for callers that
+ * cannot allocate (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): the split-K partial sums go to a fixed 64 MiB
+ * device array inside the library instead of a caller workspace. The call
+ * allocates nothing (no hipMalloc, no hipFree, no allocating library routine).
+ *
+ *   parts   0: the library's choice among the part counts whose partial sums
+ *           (parts * M * N * 4 bytes) fit in 64 MiB (1 when none does);
+ *           1: single pass; 2..64 (and at most K / 128): exactly that many,
+ *           rejected with W8A8_ERR_INVALID_ARGUMENT if they do not fit.
+ * Other arguments, requirements and errors as w8a8_gemm_postscale_ex.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind; each split call writes every partial sum it reads, so nothing needs
+ * clearing. Calls that overlap on one GPU (other streams or threads) race on
+ * the array: the caller serialises them. The array is looked up once per
+ * device on the first call that needs it.
+ */
+w8a8_status_t w8a8_gemm_postscale_noalloc(const int8_t* a, int64_t lda, const int8_t* w,
+                                          int64_t ldw, const float* a_scale,
+                                          const float* w_scale, const uint16_t* bias,
+                                          int32_t flags, uint16_t* out, int64_t ldo,
+                                          int64_t M, int64_t N, int64_t K, int32_t parts,
+                                          void* stream);
+
+/*
  * w8a8_gemm_blockwise -- blockwise-scaled W8A8 GEMM (the original
  * TurboDiffusion scheme, "Differences From TurboDiffusion", W8A8 kernel row).
  *

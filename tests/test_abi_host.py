@@ -39,7 +39,8 @@ def test_library_exports_every_declared_symbol():
                           "w8a8_gemm_postscale_gelu",
                           "w8a8_gemm_blockwise", "w8a8_gemm_i32", "w8a8_status_string",
                           "w8a8_last_error", "w8a8_version", "w8a8_gemm_splitk_parts",
-                          "w8a8_gemm_postscale_ex", "w8a8_gemm_postscale_workspace_size"}
+                          "w8a8_gemm_postscale_ex", "w8a8_gemm_postscale_workspace_size",
+                          "w8a8_gemm_postscale_noalloc"}
     raw = ctypes.CDLL(w8.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n

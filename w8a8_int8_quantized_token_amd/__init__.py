@@ -18,6 +18,7 @@ __all__ = [
     "W8A8Error", "W8A8Unsupported", "lib", "LIB_PATH", "EXPORTED_SYMBOLS",
     "w8a8_quant_rows", "w8a8_rmsnorm_quant", "w8a8_layernorm_quant", "w8a8_gemm_postscale",
     "w8a8_gemm_blockwise", "w8a8_gemm_i32", "w8a8_version", "splitk_parts",
+    "w8a8_gemm_postscale_noalloc",
     "postscale_workspace_size", "Int8Linear",
     "replace_linear_with_int8",
 ]
@@ -65,6 +66,8 @@ _SIGS = {
     "w8a8_gemm_i32": [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p],
     "w8a8_gemm_postscale_ex": [_p, _i64, _p, _i64, _p, _p, _p, ctypes.c_int32, _p, _i64, _i64,
                                _i64, _i64, ctypes.c_int32, _p, _i64, _p],
+    "w8a8_gemm_postscale_noalloc": [_p, _i64, _p, _i64, _p, _p, _p, ctypes.c_int32, _p, _i64,
+                                    _i64, _i64, _i64, ctypes.c_int32, _p],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -319,6 +322,29 @@ def w8a8_gemm_postscale(a: torch.Tensor, w: torch.Tensor, a_scale: torch.Tensor,
                                      _ptr(out), _ld(out), M, N, K, int(parts), _ptr(workspace),
                                      ws_bytes, _stream(stream))
     _check(st, "w8a8_gemm_postscale_ex")
+    return out
+
+
+def w8a8_gemm_postscale_noalloc(a: torch.Tensor, w: torch.Tensor, a_scale: torch.Tensor,
+                                w_scale: torch.Tensor, out: torch.Tensor, stream=None,
+                                bias: torch.Tensor | None = None, gelu: bool = False,
+                                parts: int = 0):
+    """The post-scale GEMM family without any allocation: split-K partial sums
+    go to the library's fixed 64 MiB device array (calls that overlap on one
+    GPU race on it). `out` must be given."""
+    if out is None:
+        _bad("out must be given (this call allocates nothing)")
+    M, N, K, out = _gemm_args(a, w, out, torch.bfloat16)
+    _vec(a_scale, torch.float32, M, "a_scale")
+    _vec(w_scale, torch.float32, N, "w_scale")
+    if bias is not None:
+        _vec(bias, torch.bfloat16, N, "bias")
+    _on_device(a.device, a=a, w=w, out=out, a_scale=a_scale, w_scale=w_scale, bias=bias)
+    st = _lib.w8a8_gemm_postscale_noalloc(_ptr(a), _ld(a), _ptr(w), _ld(w), _ptr(a_scale),
+                                          _ptr(w_scale), _ptr(bias),
+                                          W8A8_EPILOGUE_GELU if gelu else 0, _ptr(out), _ld(out),
+                                          M, N, K, int(parts), _stream(stream))
+    _check(st, "w8a8_gemm_postscale_noalloc")
     return out
 
 

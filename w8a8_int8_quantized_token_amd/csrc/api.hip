@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "launch.hpp"
@@ -156,6 +157,36 @@ w8a8_status_t postscale_call(const char* name, const int8_t* a, int64_t lda, con
                   name);
 }
 
+// Scratch memory of w8a8_gemm_postscale_noalloc: the split-K partial sums
+// of callers that cannot allocate. Each device holds its own copy for as long
+// as the library is loaded. In host code `scratch` only names the symbol; its
+// device address on the current device comes from scratch_address().
+constexpr int64_t kScratchBytes = (int64_t)64 << 20;
+static __device__ __align__(256) int8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current.
+hipError_t scratch_address(void** addr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -303,6 +334,37 @@ w8a8_status_t w8a8_gemm_postscale_ex(const int8_t* a, int64_t lda, const int8_t*
   return postscale_call("w8a8_gemm_postscale_ex launch", a, lda, w, ldw, a_scale, w_scale, bias,
                         (flags & W8A8_EPILOGUE_GELU) != 0, out, ldo, M, N, K, parts, workspace,
                         workspace_bytes, stream);
+}
+
+w8a8_status_t w8a8_gemm_postscale_noalloc(const int8_t* a, int64_t lda, const int8_t* w,
+                                          int64_t ldw, const float* a_scale,
+                                          const float* w_scale, const uint16_t* bias,
+                                          int32_t flags, uint16_t* out, int64_t ldo, int64_t M,
+                                          int64_t N, int64_t K, int32_t parts, void* stream) {
+  if (flags & ~W8A8_EPILOGUE_GELU) return fail(W8A8_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", (unsigned)flags);
+  w8a8_status_t st = check_gemm_common(a, lda, w, ldw, out, ldo, 2, M, N, K);
+  if (st != W8A8_OK) return st;
+  if (resolve_parts(M, N, K, parts) < 0)
+    return fail(W8A8_ERR_INVALID_ARGUMENT, "parts must be 0 (library's choice) or 1..%d and at most K/128",
+                w8a8::kMaxSplitParts);
+  if (M == 0) return ok();
+  // the library's own choice only considers splits whose partial sums fit the
+  // scratch; a split the caller asks for must fit it
+  const int run = parts > 0 ? parts
+                            : w8a8::splitk_parts(M, N, K, w8a8::device_cu_count(), kScratchBytes);
+  void* ws = nullptr;
+  if (run > 1) {
+    if (M * N > ((int64_t)1 << 50) || (int64_t)run * M * N * 4 > kScratchBytes)
+      return fail(W8A8_ERR_INVALID_ARGUMENT,
+                  "%d parts of %lld x %lld partial sums exceed the %lld-byte scratch of "
+                  "w8a8_gemm_postscale_noalloc (use w8a8_gemm_postscale_ex with a workspace)",
+                  run, (long long)M, (long long)N, (long long)kScratchBytes);
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return from_hip(e, "w8a8_gemm_postscale_noalloc scratch lookup");
+  }
+  return postscale_call("w8a8_gemm_postscale_noalloc launch", a, lda, w, ldw, a_scale, w_scale,
+                        bias, (flags & W8A8_EPILOGUE_GELU) != 0, out, ldo, M, N, K, run, ws,
+                        run > 1 ? kScratchBytes : 0, stream);
 }
 
 int64_t w8a8_gemm_postscale_workspace_size(int64_t M, int64_t N, int64_t K, int32_t parts) {

@@ -71,8 +71,9 @@ constexpr int64_t kMaxSplitWorkspace = (int64_t)1 << 30;
 // K parts for a post-scale GEMM of this shape on `cus` compute units, from a
 // cost model of the split (fewer stages per work item against a per-item
 // cost, the partial sums' traffic, a fixed cost and the host's floor); 1
-// unless splitting saves 15% of the time. A pure function of its arguments.
-int splitk_parts(int64_t M, int64_t N, int64_t K, int cus);
+// unless splitting saves 15% of the time. Only part counts whose partial sums
+// fit max_ws bytes are considered. A pure function of its arguments.
+int splitk_parts(int64_t M, int64_t N, int64_t K, int cus, int64_t max_ws = kMaxSplitWorkspace);
 
 // Persistent pipelined kernel with per-K-block scales.
 hipError_t launch_gemm_blockwise(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,

@@ -89,7 +89,7 @@ hipError_t launch_splitk_postscale(const int32_t* ws, int splits, int64_t M, int
   return hipGetLastError();
 }
 
-int splitk_parts(int64_t M, int64_t N, int64_t K, int cus) {
+int splitk_parts(int64_t M, int64_t N, int64_t K, int cus, int64_t max_ws) {
   const int64_t nk = K / 128;
   const int64_t bytes_per_part = M * N * 4;
   // Cost model in microseconds, fitted to timings of split and single passes
@@ -112,7 +112,7 @@ int splitk_parts(int64_t M, int64_t N, int64_t K, int cus) {
   double best_us = 0.0;
   int64_t last = 1;
   for (int64_t parts = 2; parts <= nk && parts <= kMaxSplitParts; ++parts) {
-    if (parts * bytes_per_part > kMaxSplitWorkspace) break;
+    if (parts * bytes_per_part > max_ws) break;
     const double rounds = (double)((tiles * parts + cus - 1) / cus);
     double us = rounds * ((double)((nk + parts - 1) / parts) * stage_us + item_us) + fixed_us +
                 us_per_byte * (double)(parts * bytes_per_part);
