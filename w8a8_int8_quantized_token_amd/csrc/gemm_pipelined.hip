@@ -52,7 +52,8 @@ constexpr int kSlots = 2;             // LDS ring of stages
 constexpr int kSlotBytes = (kBN + kBM) * kBK;   // 64 KiB
 constexpr int kWaves = 8, kThreads = kWaves * kWave;
 constexpr int kTN = 8, kTM = 4;       // 16x16 MFMA tiles per wave: 128 channels x 64 tokens
-constexpr int kLoads = (kBN + kBM) * kBK / 1024 / kWaves;   // 1 KiB wave-loads per stage: 8
+constexpr int kLoaderWaves = 4;       // waves that issue the stage refills (one per SIMD)
+constexpr int kLoads = (kBN + kBM) * kBK / 1024 / kLoaderWaves;   // 1 KiB wave-loads per loader wave
 constexpr int kStoresPerTile = kTM * 4;                       // 16-byte stores per wave per tile
 constexpr int kScaleBytes = (kBN + kBM) * 4;   // one tile's scales
 constexpr int kBiasBytes = kWaves * 256;       // one dword wave-load per wave (the tile's
@@ -179,10 +180,15 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1;
 
-  // ---- loader: wave-load g fills stage rows 8 (wave + 8 g) + [0, 8) (g < 4:
-  // weight rows, g >= 4: activation rows); lane -> row r_l + 64 g', physical
-  // chunk lane % 8, logical chunk fixed per lane (keys ignore bits >= 6).
-  const int r_l = 8 * wave + (lane >> 3);
+  // ---- loader: only waves 0 .. kLoaderWaves-1 refill the ring (one per SIMD:
+  // issuing the refills stalls the issuing wave, and the other wave of its
+  // SIMD keeps the MFMAs fed meanwhile). Loader wave v's wave-load g fills
+  // stage rows 8 (v + kLoaderWaves g) + [0, 8) of the weight half and then of
+  // the activation half; lane -> row r_l + 8 kLoaderWaves g, physical chunk
+  // lane % 8, logical chunk fixed per lane (the keys ignore row bits >= 5).
+  constexpr int kRowStep = 8 * kLoaderWaves;
+  const bool loader = wave < kLoaderWaves;
+  const int r_l = 8 * (wave % kLoaderWaves) + (lane >> 3);
   const int p = lane & 7;
   const int cw = (p ^ key_w(r_l)) << 4, ca = (p ^ key_a(r_l)) << 4;
   // The tile's weight and activation row blocks as buffers. Full tiles: a
@@ -207,29 +213,30 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   };
   load_tile(0);
   auto issue_next = [&](int slot) {
-    int8_t* dst = lds + slot * kSlotBytes + wave * 1024;
+    if (!loader) return;
+    int8_t* dst = lds + slot * kSlotBytes + (wave % kLoaderWaves) * 1024;
     const int koff = ld_kt * kBK;
 #pragma unroll
     for (int g = 0; g < kLoads / 2; ++g) {
-      const int r = r_l + 64 * g;
+      const int r = r_l + kRowStep * g;
       if constexpr (kFull)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_w, (lds_void*)(dst + g * kWaves * 1024), 16,
-                                                 vo_w, koff + 64 * g * (int)ldw, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_w, (lds_void*)(dst + g * kRowStep * kBK), 16,
+                                                 vo_w, koff + kRowStep * g * (int)ldw, 0, 0);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_w, (lds_void*)(dst + g * kWaves * 1024), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_w, (lds_void*)(dst + g * kRowStep * kBK), 16,
                                                  (r < ld_rvn ? r : ld_rvn) * (int)ldw + cw, koff,
                                                  0, 0);
     }
 #pragma unroll
     for (int g = 0; g < kLoads / 2; ++g) {
-      const int r = r_l + 64 * g;
+      const int r = r_l + kRowStep * g;
       if constexpr (kFull)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_a,
-                                                 (lds_void*)(dst + kBN * kBK + g * kWaves * 1024),
-                                                 16, vo_a, koff + 64 * g * (int)lda, 0, 0);
+                                                 (lds_void*)(dst + kBN * kBK + g * kRowStep * kBK),
+                                                 16, vo_a, koff + kRowStep * g * (int)lda, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_a,
-                                                 (lds_void*)(dst + kBN * kBK + g * kWaves * 1024),
+                                                 (lds_void*)(dst + kBN * kBK + g * kRowStep * kBK),
                                                  16, (r < ld_rvm ? r : ld_rvm) * (int)lda + ca,
                                                  koff, 0, 0);
     }
@@ -458,7 +465,7 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   issue_next(0);
   advance_loader();
   issue_next(1);
-  wait_vmcnt_le(kLoads);                 // stage 0 landed
+  wait_vmcnt_le(loader ? kLoads : 0);    // stage 0 landed
   lds_barrier();
   read_frags(f0, 0, 0);
 
