@@ -41,16 +41,20 @@ constexpr int kWaves = 8, kThreads = kWaves * kWave;
 constexpr int kTN = 4, kTM = 4;       // 16x16 MFMA tiles per wave: 64 channels x 64 tokens
 constexpr int kHalf = kTN / 2;        // tiles i < kHalf are rescaled in their own stage
 constexpr int kTileBytes = (kBN + kBM) * kBK;          // 48 KiB of codes per stage
-constexpr int kScaleArea = kWaves * 256;               // one dword wave-load per wave
+// Waves 0-3 (one per SIMD) issue all of a stage's loads; issuing them stalls
+// the issuing wave, and the other wave of its SIMD keeps the MFMAs fed.
+constexpr int kLoaderWaves = 4;
+constexpr int kScaleArea = kLoaderWaves * 256;         // one dword wave-load per loader wave
 constexpr int kSlotBytes = kTileBytes + kScaleArea;
-constexpr int kLoads = kTileBytes / 1024 / kWaves;     // 1 KiB code wave-loads per wave: 6
+constexpr int kLoads = kTileBytes / 1024 / kLoaderWaves;   // 1 KiB code wave-loads per loader: 12
 constexpr int kStageLoads = kLoads + 1;                // plus the scale wave-load
+constexpr int kRowStep = 8 * kLoaderWaves;             // rows between a loader's wave-loads
 constexpr int kStoresPerTile = kTM * 2;                // 16-byte stores per wave per tile
 constexpr int kGroupM = 8;
 // Three slots (150 KiB of LDS) keep two stages in flight behind the one being
 // consumed; two slots also work and measured about 4% slower.
 constexpr int kRingSlots = 3;
-static_assert(kLoads == kBN / 64 + kBM / 64, "code rows split evenly over the waves");
+static_assert(kLoads == kBN / kRowStep + kBM / kRowStep, "code rows split evenly over the loaders");
 
 // Swizzle keys of the 128-byte LDS rows (logical 16-byte chunk c of row r at
 // c ^ key(r)). A wave's weight rows are read in the permuted slot order
@@ -74,9 +78,11 @@ void gemm_i8_blockwise(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave & 3, wm = wave >> 2;
 
-  // ---- loader: code wave-load g fills stage rows 64 g + r_l (g < 4: weight
-  // rows, g >= 4: activation rows), lane -> physical chunk lane % 8.
-  const int r_l = 8 * wave + (lane >> 3);
+  // ---- loader (waves 0-3): code wave-load g fills stage rows kRowStep g + r_l
+  // of the weight rows, then of the activation rows; lane -> physical chunk
+  // lane % 8 (the keys ignore row bits >= 5).
+  const bool loader = wave < kLoaderWaves;
+  const int r_l = 8 * (wave % kLoaderWaves) + (lane >> 3);
   const int p = lane & 7;
   const int cw = (p ^ key_w(r_l)) << 4, ca = (p ^ key_a(r_l)) << 4;
   int ld_k = 0, ld_kt = 0, ld_rvn = 0, ld_rvm = 0, ld_vs = 0;
@@ -106,20 +112,21 @@ void gemm_i8_blockwise(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
   };
   load_tile(0);
   auto issue_next = [&](int slot) {
-    int8_t* dst = lds + slot * kSlotBytes + wave * 1024;
+    if (!loader) return;
+    int8_t* dst = lds + slot * kSlotBytes + (wave % kLoaderWaves) * 1024;
     const int koff = ld_kt * kBK;
 #pragma unroll
-    for (int g = 0; g < kBN / 64; ++g) {
-      const int r = r_l + 64 * g;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_w, (lds_void*)(dst + g * kWaves * 1024), 16,
+    for (int g = 0; g < kBN / kRowStep; ++g) {
+      const int r = r_l + kRowStep * g;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_w, (lds_void*)(dst + g * kRowStep * kBK), 16,
                                                (r < ld_rvn ? r : ld_rvn) * (int)ldw + cw, koff,
                                                0, 0);
     }
 #pragma unroll
-    for (int g = 0; g < kBM / 64; ++g) {
-      const int r = r_l + 64 * g;
+    for (int g = 0; g < kBM / kRowStep; ++g) {
+      const int r = r_l + kRowStep * g;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_a,
-                                               (lds_void*)(dst + kBN * kBK + g * kWaves * 1024),
+                                               (lds_void*)(dst + kBN * kBK + g * kRowStep * kBK),
                                                16, (r < ld_rvm ? r : ld_rvm) * (int)lda + ca,
                                                koff, 0, 0);
     }
@@ -225,7 +232,7 @@ void gemm_i8_blockwise(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
     if (i > 0) advance_loader();
     issue_next(i);
   }
-  wait_vmcnt_le(kStageLoads * (kSlots - 1));   // stage 0 landed
+  if (loader) wait_vmcnt<kStageLoads * (kSlots - 1)>();   // stage 0 landed
   lds_barrier();
   read_frags(f0, 0, 0);
 
@@ -272,7 +279,10 @@ void gemm_i8_blockwise(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
                    : "memory");
       // (the loads of the kSlots - 2 stages after it and the previous tile's
       // stores may still be in flight)
-      wait_vmcnt_le(kStageLoads * (kSlots - 2) + pending_stores);
+      if (loader) {
+        if (pending_stores) wait_vmcnt<kStageLoads * (kSlots - 2) + kStoresPerTile>();
+        else wait_vmcnt<kStageLoads * (kSlots - 2)>();
+      }
       lds_barrier();                       // ... for every wave; slot `slot` is free
       __builtin_amdgcn_sched_barrier(0);
       pending_stores = 0;
@@ -293,11 +303,10 @@ void gemm_i8_blockwise(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
 #pragma unroll
         for (int j = 0; j < kTM; ++j) rescale(i, j, s_cur[j]);
 #pragma unroll
-      for (int q = 0; q < kStageLoads; ++q) {
+      for (int q = 0; q < kHalf * kTM; ++q) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kHalf * kTM - kStageLoads, 0);
 #pragma unroll
       for (int q = 0; q < (kTN - kHalf) * kTM; ++q) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);

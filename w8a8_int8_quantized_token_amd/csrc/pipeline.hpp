@@ -37,6 +37,13 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// s_waitcnt vmcnt(N) for a compile-time N.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // A workgroup's work items: logical ids start + k * stride, k < count. Workgroup
 // b runs on XCD b % 8; each XCD owns a contiguous range of logical ids, so
 // the rows its tiles share stay in that XCD's L2. Items default to the tiles;
