@@ -12,6 +12,8 @@ timed separately and reported, not part of a step):
   square               per-token quant [4096 x 4096] -> GEMM vs W [4096 x 4096]
   blockwise_small/large  1x128 quant [1000|32760 x 5120] -> blockwise GEMM vs
                        128x128-quantised W [5120 x 5120]
+  m1000                per-token quant [1000 x 5120] -> GEMM vs W [5120 x 5120]
+  (also ln_up_proj, up_proj_gelu, small_m: see workloads/)
 
 Prints ONE JSON line: whole-step INT8 throughput (TOP/s, 2*M*N*K ops per
 step), the per-kernel roofline of the dominant kernel (the GEMM, against the
@@ -36,8 +38,8 @@ METRIC = "W8A8 GEMM INT8 TOPS + % INT8 MFMA peak at DiT FFN shapes; quant GB/s"
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, TOP/s
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 N_ROTATE = 3                   # activation buffers cycled so inputs come from HBM
-GEMM_SOURCES = ("gemm.hip", "gemm_pipelined.hip", "gemm_blockwise.hip", "splitk.hip", "pipeline.hpp",
-                "device_common.hpp", "launch.hpp")
+GEMM_SOURCES = ("gemm.hip", "gemm_pipelined.hip", "gemm_blockwise.hip", "gemm_tile160.hip",
+                "splitk.hip", "pipeline.hpp", "device_common.hpp", "launch.hpp")
 
 
 def parse():
@@ -345,7 +347,7 @@ def main():
         quant_bytes = 3 * M * K + 4 * M
 
     if wl.blockwise:
-        gemm_name = "gemm_blockwise"
+        gemm_name = "gemm_blockwise" + ("_t160" if w8.tile_channels(M, N, K, True) == 160 else "")
         def gemm():
             w8.w8a8_gemm_blockwise(qa, qw, sa, sw, out=out)
     else:
@@ -353,7 +355,8 @@ def main():
         # (few tokens), its two passes all count as the GEMM
         gemm_name = ("gemm_postscale" + ("_bias" if bias is not None else "")
                      + ("_gelu" if wl.gelu else "")
-                     + ("_splitk" if w8.splitk_parts(M, N, K) > 1 else ""))
+                     + ("_splitk" if w8.splitk_parts(M, N, K) > 1 else
+                        ("_t160" if w8.tile_channels(M, N, K) == 160 else "")))
         def gemm():
             w8.w8a8_gemm_postscale(qa, qw, sa, sw, out=out, bias=bias, gelu=wl.gelu)
 

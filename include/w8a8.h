@@ -346,6 +346,20 @@ const char* w8a8_version(void);
  */
 int32_t w8a8_gemm_splitk_parts(int64_t M, int64_t N, int64_t K);
 
+/*
+ * w8a8_gemm_tile_channels -- the output-channel width of the tiles a single
+ * pass of the post-scale family (blockwise = 0) or of w8a8_gemm_blockwise
+ * (blockwise = 1) uses for an M x N x K GEMM on the current device: 256 (the
+ * persistent kernels: 256 x 256 post-scale tiles, 256-channel x 128-token
+ * blockwise tiles) or 160 (128-token x 160-channel tiles, one workgroup per
+ * tile, chosen for few tokens where the larger tiles would leave compute
+ * units idle). The results are identical either way. -1 for a shape the INT8
+ * path rejects. Host only, launches nothing. Passage: "Differences From
+ * TurboDiffusion", W8A8-kernel row (the kernels serve the LTX shapes, and
+ * other selected Linears).
+ */
+int32_t w8a8_gemm_tile_channels(int64_t M, int64_t N, int64_t K, int32_t blockwise);
+
 #ifdef __cplusplus
 }
 #endif

@@ -44,11 +44,19 @@ WORKLOAD_SHAPES = {
     "ln_up_proj": "M=28672 N=16384 K=4096 (LayerNorm+modulation+quant -> post-scale GEMM)",
     "up_proj_gelu": "M=28672 N=16384 K=4096 (RMSNorm+quant -> post-scale GEMM + bias + GELU)",
     "small_m": "M=256 N=5120 K=13824 (quant -> split-K: INT32 partial sums + post-scale pass)",
+    "m1000": "M=1000 N=5120 K=5120 (quant -> post-scale GEMM on 128 x 160 tiles)",
     "tiny": "M=64 N=128 K=256",
 }
 
 
 def short_name(kernel: str) -> str:
+    if "gemm_i8_t160_blockwise" in kernel:
+        return "gemm_blockwise_t160"
+    if "gemm_i8_t160_postscale" in kernel:
+        m = re.search(r"Epilogue\)(\d)|EpilogueE(\d)", kernel)
+        e = (m.group(1) or m.group(2)) if m else "?"
+        return {"0": "gemm_postscale_t160", "3": "gemm_postscale_bias_t160",
+                "4": "gemm_postscale_gelu_t160", "5": "gemm_postscale_bias_gelu_t160"}.get(e, "gemm_t160")
     if "gemm_i8_blockwise" in kernel:
         return "gemm_blockwise"
     if "gemm_i8_" in kernel:

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
                           "w8a8_gemm_blockwise", "w8a8_gemm_i32", "w8a8_status_string",
                           "w8a8_last_error", "w8a8_version", "w8a8_gemm_splitk_parts",
                           "w8a8_gemm_postscale_ex", "w8a8_gemm_postscale_workspace_size",
-                          "w8a8_gemm_postscale_noalloc"}
+                          "w8a8_gemm_postscale_noalloc", "w8a8_gemm_tile_channels"}
     raw = ctypes.CDLL(w8.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -258,15 +258,35 @@ def test_splitk_parts_query():
     assert w8.splitk_parts(28672, 16384, 4096) == 1          # tiles fill the chip
     assert w8.splitk_parts(1000, 5120, 5120) == 1            # partial sums would cost more
     assert w8.splitk_parts(129, 5120, 13824) > 1
-    # the cost model's measured calls: split where a sweep on MI355X showed a
-    # saving (512 x 4096 x 4096: 35 against 42 us), not where it showed none
-    assert w8.splitk_parts(512, 4096, 4096) > 1
+    # the cost model's measured calls (MI355X, GPU time of graph-replayed
+    # calls): split where that was faster than the better single pass
+    # (129 x 5120 x 13824: 31 us in 8 parts against 48 us on 128 x 160
+    # tiles), not where one pass on 128 x 160 tiles was (512 x 4096 x 4096:
+    # 19.6 us against 28.8 us in 4 parts)
+    assert w8.splitk_parts(512, 4096, 4096) == 1
     assert w8.splitk_parts(1024, 4096, 4096) == 1 and w8.splitk_parts(256, 16384, 4096) == 1
     assert 4 <= w8.splitk_parts(256, 5120, 13824) <= 16
     assert w8.splitk_parts(0, 128, 256) == 1 and w8.splitk_parts(4, 128, 0) == 1
     for M, N, K in ((1, 256, 2048), (256, 5120, 13824), (33, 128, 8192)):
         p = w8.splitk_parts(M, N, K)
         assert 1 <= p <= K // 128 and p * M * N * 4 <= 1 << 30
+
+
+def test_tile_channels_query():
+    # no GPU here: the model runs with its 256-unit default. Few tokens take
+    # 128 x 160 tiles (measured: 1000 x 5120 x 5120 in 28.8 against 50 us),
+    # shapes whose 256 x 256 tiles fill the chip keep them
+    assert w8.tile_channels(1000, 5120, 5120) == 160
+    assert w8.tile_channels(1000, 5120, 5120, blockwise=True) == 160
+    assert w8.tile_channels(512, 4096, 4096) == 160
+    assert w8.tile_channels(28672, 16384, 4096) == 256
+    assert w8.tile_channels(32760, 5120, 13824) == 256
+    assert w8.tile_channels(4096, 4096, 4096) == 256
+    assert w8.tile_channels(2048, 5120, 5120) == 256            # two rounds of 128 x 160 tiles
+    assert w8.tile_channels(4096, 5120, 5120, blockwise=True) == 256
+    assert w8.tile_channels(0, 128, 128) == 256
+    assert w8.tile_channels(64, 100, 256) == -1 and w8.tile_channels(64, 128, 200) == -1
+    assert w8.lib().w8a8_gemm_tile_channels(64, 128, 256, 2) == -1
 
 
 def test_workspace_size_query():

@@ -47,7 +47,8 @@ def exact_check(got, ref, what):
 
 
 @pytest.mark.parametrize("name", ["square", "up_proj", "down_proj", "blockwise_small",
-                                  "blockwise_large", "ln_up_proj", "up_proj_gelu", "small_m"])
+                                  "blockwise_large", "ln_up_proj", "up_proj_gelu", "small_m",
+                                  "m1000"])
 def test_workload_full_size(name):
     wl = W.WORKLOADS[name]
     M, N, K = wl.M, wl.N, wl.K
@@ -86,7 +87,8 @@ def test_workload_full_size(name):
         out = w8.w8a8_gemm_blockwise(qa, qw, sa, sw)
     else:
         parts = w8.splitk_parts(M, N, K)
-        log(f"  post-scale GEMM: bias={bias is not None} gelu={wl.gelu} K parts {parts}")
+        log(f"  post-scale GEMM: bias={bias is not None} gelu={wl.gelu} K parts {parts} "
+            f"tile channels {w8.tile_channels(M, N, K)}")
         if name == "small_m":
             assert parts > 1
         out = w8.w8a8_gemm_postscale(qa, qw, sa, sw, bias=None if bias is None else bf16_to_dev(bias),

@@ -313,7 +313,18 @@ def test_gemm_postscale(shape, seed):
 BLOCKWISE_SHAPES = [((64, 128, 256), 61), ((1000, 5120, 5120), 62), ((300, 256, 384), 63),
                     ((1, 128, 128), 64), ((257, 640, 1024), 65),
                     # more tiles than CUs, ragged M, N % 256 == 128
-                    ((8292, 1152, 256), 67), ((4100, 4096, 384), 68), ((129, 384, 13824), 69)]
+                    ((8292, 1152, 256), 67), ((4100, 4096, 384), 68), ((129, 384, 13824), 69),
+                    # 128 x 160 tiles (few tokens, long K): N % 160 = 0, 32 and 96
+                    ((300, 2560, 8192), 70), ((200, 1152, 8192), 71), ((100, 4096, 8192), 72)]
+
+
+def test_parity_shapes_cover_both_tilings():
+    # the shape lists must keep exercising both the 256-channel and the
+    # 128 x 160 kernels (the library picks by a cost model, for 256 CUs here)
+    post = [w8.tile_channels(*s) for s, _ in GEMM_SHAPES if w8.splitk_parts(*s) == 1]
+    block = [w8.tile_channels(*s, blockwise=True) for s, _ in BLOCKWISE_SHAPES]
+    assert post.count(160) >= 3 and post.count(256) >= 3, post
+    assert block.count(160) >= 3 and block.count(256) >= 3, block
 
 
 @pytest.mark.parametrize("shape,seed", BLOCKWISE_SHAPES)

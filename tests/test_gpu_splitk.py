@@ -20,20 +20,26 @@ from tests.gpu_util import bf16_from_dev, bf16_to_dev, log, to_dev
 
 pytestmark = pytest.mark.gpu
 
-# (M, N, K): small M against wide N and long K, where the library's cost model
-# splits K (parts in the comments, for 256 compute units): ragged and whole
-# tiles, parts of equal and unequal stage counts, one-stage parts
+# (M, N, K): small M against wide N and long K. The library's cost model
+# (for 256 compute units) splits K for some of them and runs others as one
+# pass (on 128 x 160 tiles, or on 256 x 256 tiles where those fill the chip);
+# every result must equal the oracle's either way. Ragged and whole tiles,
+# parts of equal and unequal stage counts.
 SPLIT_SHAPES = [((129, 5120, 13824), 132),    # 9 parts of 12 stages
-                ((64, 1024, 4096), 134),      # 4 parts of 8
+                ((64, 1024, 4096), 134),
                 ((33, 128, 8192), 137),       # 8 parts of 8
-                ((1, 5120, 5120), 138),       # 5 parts of 8
-                ((100, 2048, 3200), 139),     # 4 parts of 6 or 7 stages
-                ((300, 768, 5248), 140),      # 6 parts of 6 or 7; full-tile mode
+                ((1, 5120, 5120), 138),
+                ((100, 2048, 3200), 139),
+                ((300, 768, 5248), 140),
                 ((77, 384, 11136), 145),      # 10 parts of 8 or 9
                 ((512, 1280, 8192), 146),     # 8 parts of 8; full-tile mode
-                # not split (the tiles fill the chip, or the partial sums cost
-                # more than they save): the single pass, same bar
                 ((1000, 5120, 5120), 131), ((257, 640, 1024), 133)]
+
+
+def test_split_shapes_cover_both_paths():
+    # the list above must keep exercising split-K and the single pass
+    parts = [w8.splitk_parts(*shape) for shape, _ in SPLIT_SHAPES]
+    assert sum(p > 1 for p in parts) >= 4 and sum(p == 1 for p in parts) >= 3, parts
 
 
 @pytest.mark.parametrize("with_bias", [False, True])

@@ -18,7 +18,7 @@ __all__ = [
     "W8A8Error", "W8A8Unsupported", "lib", "LIB_PATH", "EXPORTED_SYMBOLS",
     "w8a8_quant_rows", "w8a8_rmsnorm_quant", "w8a8_layernorm_quant", "w8a8_gemm_postscale",
     "w8a8_gemm_blockwise", "w8a8_gemm_i32", "w8a8_version", "splitk_parts",
-    "w8a8_gemm_postscale_noalloc",
+    "w8a8_gemm_postscale_noalloc", "tile_channels",
     "postscale_workspace_size", "Int8Linear",
     "replace_linear_with_int8",
 ]
@@ -83,9 +83,12 @@ _lib.w8a8_gemm_splitk_parts.argtypes = [_i64, _i64, _i64]
 _lib.w8a8_gemm_splitk_parts.restype = ctypes.c_int32
 _lib.w8a8_gemm_postscale_workspace_size.argtypes = [_i64, _i64, _i64, ctypes.c_int32]
 _lib.w8a8_gemm_postscale_workspace_size.restype = _i64
+_lib.w8a8_gemm_tile_channels.argtypes = [_i64, _i64, _i64, ctypes.c_int32]
+_lib.w8a8_gemm_tile_channels.restype = ctypes.c_int32
 
 EXPORTED_SYMBOLS = tuple(_SIGS) + ("w8a8_status_string", "w8a8_last_error", "w8a8_version",
-                                   "w8a8_gemm_splitk_parts", "w8a8_gemm_postscale_workspace_size")
+                                   "w8a8_gemm_splitk_parts", "w8a8_gemm_postscale_workspace_size",
+                                   "w8a8_gemm_tile_channels")
 
 
 def lib() -> ctypes.CDLL:
@@ -95,6 +98,12 @@ def lib() -> ctypes.CDLL:
 
 def w8a8_version() -> str:
     return _lib.w8a8_version().decode()
+
+
+def tile_channels(M: int, N: int, K: int, blockwise: bool = False) -> int:
+    """Output-channel width of the tiles a single pass uses on the current
+    device: 256 (persistent kernels) or 160 (128 x 160 tiles); -1 if rejected."""
+    return int(_lib.w8a8_gemm_tile_channels(M, N, K, 1 if blockwise else 0))
 
 
 def splitk_parts(M: int, N: int, K: int) -> int:

@@ -205,6 +205,14 @@ const char* w8a8_last_error(void) { return g_last_error.c_str(); }
 
 const char* w8a8_version(void) { return "w8a8-gfx950 0.1"; }
 
+int32_t w8a8_gemm_tile_channels(int64_t M, int64_t N, int64_t K, int32_t blockwise) {
+  if (M < 0 || N < 128 || N % 128 || K < 128 || K % 128 || K > W8A8_MAX_K || M > kMaxRows ||
+      N > kMaxRows || (blockwise != 0 && blockwise != 1))
+    return -1;
+  if (M == 0) return 256;
+  return w8a8::use_tile160(M, N, K, w8a8::device_cu_count(), blockwise != 0) ? 160 : 256;
+}
+
 int32_t w8a8_gemm_splitk_parts(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K < 128) return 1;
   return w8a8::splitk_parts(M, N, K, w8a8::device_cu_count());

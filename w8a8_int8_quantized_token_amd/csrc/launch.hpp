@@ -75,6 +75,23 @@ constexpr int64_t kMaxSplitWorkspace = (int64_t)1 << 30;
 // fit max_ws bytes are considered. A pure function of its arguments.
 int splitk_parts(int64_t M, int64_t N, int64_t K, int cus, int64_t max_ws = kMaxSplitWorkspace);
 
+// 128-token x 160-channel tiles, one workgroup per tile (gemm_tile160.hip):
+// the post-scale epilogues (bias, GELU) and the blockwise one. N % 128 == 0.
+hipError_t launch_gemm_tile160(Epilogue epi, const int8_t* a, int64_t lda, const int8_t* w,
+                               int64_t ldw, const float* a_scale, const float* w_scale,
+                               const uint16_t* bias, uint16_t* out, int64_t ldo, int64_t M,
+                               int64_t N, int64_t K, hipStream_t st);
+int tile160_tiles(int64_t M, int64_t N);
+
+// Estimated microseconds of one pass of the persistent kernels (256 x 256
+// post-scale tiles, 256 x 128 blockwise tiles) and of the 128 x 160 kernel on
+// `cus` compute units, and the choice between them: a single pass uses
+// 128 x 160 tiles when that is estimated at least 10% faster (few tokens:
+// the larger tiles leave compute units idle).
+double single_pass_us_256(int64_t M, int64_t N, int64_t K, int cus, bool blockwise);
+double single_pass_us_160(int64_t M, int64_t N, int64_t K, int cus, bool blockwise);
+bool use_tile160(int64_t M, int64_t N, int64_t K, int cus, bool blockwise);
+
 // Persistent pipelined kernel with per-K-block scales.
 hipError_t launch_gemm_blockwise(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
                                  const float* a_scale, const float* w_scale, uint16_t* out,

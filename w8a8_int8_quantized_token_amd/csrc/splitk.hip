@@ -95,8 +95,7 @@ int splitk_parts(int64_t M, int64_t N, int64_t K, int cus, int64_t max_ws) {
   // Cost model in microseconds, fitted to timings of split and single passes
   // on MI355X (M from 64 to 2048, N from 1024 to 16384, K from 4096 to 13824,
   // 1 to 24 parts):
-  //  * single pass: 1.3 per 128-byte K stage of a 256 x 256 tile, per round
-  //    of tiles over the compute units;
+  //  * single pass: the better of the two tilings (gemm.hip);
   //  * split: per round of work items, 1.3 per stage plus 3 for the item's
   //    prologue and INT32 epilogue; 11 for the extra pass and the workspace;
   //    0.286 per MB of partial sums (written once, read once); and never
@@ -107,7 +106,10 @@ int splitk_parts(int64_t M, int64_t N, int64_t K, int cus, int64_t max_ws) {
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
   const double stage_us = 1.3, item_us = 3.0, fixed_us = 11.0, us_per_byte = 0.286e-6,
                floor_us = 25.0;
-  const double single = (double)((tiles + cus - 1) / cus) * nk * stage_us;
+  // the single pass on the better of its two tilings
+  const double s256 = single_pass_us_256(M, N, K, cus, false);
+  const double s160 = single_pass_us_160(M, N, K, cus, false);
+  const double single = s160 < s256 ? s160 : s256;
   double est[kMaxSplitParts + 1] = {0};
   double best_us = 0.0;
   int64_t last = 1;

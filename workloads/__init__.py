@@ -29,6 +29,8 @@ The shapes and value distributions are those of the five workloads:
                 ~N(0,0.1), GELU on the output
 * ``small_m``   X [256,13824] = BF16(GELU_erf(z)) (a short sequence against
                 the down projection's weight); W [5120,13824] ~N(0,0.01)
+* ``m1000``     X [1000,5120] ~N(0,1) (a thousand tokens); W [5120,5120]
+                ~N(0,0.02): the post-scale GEMM at the blockwise_small shape
 """
 from __future__ import annotations
 
@@ -84,6 +86,7 @@ WORKLOADS = {
     "up_proj_gelu": Workload("up_proj_gelu", 28672, 16384, 4096, 1008, "normal", 1.0, 0.02,
                              norm=True, bias_std=0.1, gelu=True),
     "small_m": Workload("small_m", 256, 5120, 13824, 1009, "gelu", 1.0, 0.01),
+    "m1000": Workload("m1000", 1000, 5120, 5120, 1010, "normal", 1.0, 0.02),
 }
 
 
