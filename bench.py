@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--preload-ms", type=float, default=250.0,
                    help="untimed load before the timed steps: at least this much wall time "
                         "(and at least --warmup steps)")
+    p.add_argument("--b2b-ms", type=float, default=20.0,
+                   help="back-to-back launches of each kernel after the timed steps: at least "
+                        "this much GPU time (and at least 10 launches)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-bf16", action="store_true", help="skip the torch BF16 Linear yardstick")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -348,7 +351,7 @@ def main():
 
     if wl.blockwise:
         gemm_name = "gemm_blockwise" + ("_t160" if w8.tile_channels(M, N, K, True) == 160 else "")
-        def gemm():
+        def gemm(_i=0):
             w8.w8a8_gemm_blockwise(qa, qw, sa, sw, out=out)
     else:
         # the epilogue's extras (bias, GELU) and, where the library splits K
@@ -357,7 +360,7 @@ def main():
                      + ("_gelu" if wl.gelu else "")
                      + ("_splitk" if w8.splitk_parts(M, N, K) > 1 else
                         ("_t160" if w8.tile_channels(M, N, K) == 160 else "")))
-        def gemm():
+        def gemm(_i=0):
             w8.w8a8_gemm_postscale(qa, qw, sa, sw, out=out, bias=bias, gelu=wl.gelu)
 
     ops = 2 * M * N * K
@@ -396,19 +399,24 @@ def main():
     step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
     ms_per_step = wall_s * 1e3 / args.steps
 
-    # The quant kernel alone, back to back over the rotated inputs between one
-    # event pair: its sustained rate, without the per-launch event gaps that
-    # the per-step pairs add to a ~60 us kernel.
-    q_reps = 30
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(q_reps):
-        quant(xs[i % N_ROTATE])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    quant_b2b_ms = e0.elapsed_time(e1) / q_reps
+    # Each kernel alone, back to back between one event pair on the launch
+    # stream, right after the timed steps: its average launch duration
+    # without the gaps that a per-launch event pair adds (a few us, which
+    # matter for kernels of tens of us). These give the roofline figures.
+    def back_to_back(fn, least=10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(least, int(args.b2b_ms / max(float(gemm_ms.mean()), 1e-3)) if fn is gemm else 30)
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps, reps
 
-    gemm_avg = float(gemm_ms.mean())
+    quant_b2b_ms, _ = back_to_back(lambda i: quant(xs[i % N_ROTATE]))
+    gemm_b2b_ms, gemm_reps = back_to_back(gemm)
+
+    gemm_avg = gemm_b2b_ms
     gemm_tops = ops / (gemm_avg * 1e-3) / 1e12
     quant_avg = float(quant_ms.mean())
     quant_gbs = quant_bytes / (quant_avg * 1e-3) / 1e9
@@ -418,7 +426,9 @@ def main():
     traffic = load_traffic(gemm_name, args.workload, gemm_hash)
 
     extra = {
-        "gemm_ms_avg": round(gemm_avg, 4), "gemm_ms_min": round(float(gemm_ms.min()), 4),
+        "gemm_ms_avg": round(gemm_avg, 4), "gemm_back_to_back_launches": gemm_reps,
+        "gemm_ms_in_step_avg": round(float(gemm_ms.mean()), 4),
+        "gemm_ms_in_step_min": round(float(gemm_ms.min()), 4),
         "gemm_tops": round(gemm_tops, 1), "gemm_frac_int8_peak": round(gemm_tops / INT8_PEAK_TOPS, 4),
         f"{quant_name}_ms_avg": round(quant_b2b_ms, 4),
         f"{quant_name}_gbs": round(quant_bytes / (quant_b2b_ms * 1e-3) / 1e9, 1),
