@@ -156,9 +156,13 @@ def test_quant_exhaustive_bf16_pairs():
 
 
 def test_rmsnorm_quant():
-    # full rows of 1, 4 and 8 vectors per lane, few and many rows
+    # full rows of 1, 3, 4, 5, 6 and 8 vectors per lane (the fp32-resident
+    # kernel), 27 and 32 (packed rows), ragged rows, few rows and more rows than
+    # the persistent grid covers in one pass
     for shape, seed in (((64, 256), 31), ((2048, 4096), 32), ((100, 13824), 33), ((5, 16384), 34),
-                        ((3, 8), 35), ((777, 2048), 36), ((3, 512), 37), ((40000, 512), 38)):
+                        ((3, 8), 35), ((777, 2048), 36), ((3, 512), 37), ((40000, 512), 38),
+                        ((70, 1536), 39), ((50, 2560), 40), ((300, 3072), 41), ((33, 1000), 42),
+                        ((5000, 4096), 43)):
         log(f"rmsnorm_quant {shape}")
         x = W.random_bits(shape, seed)
         if shape[0] >= 8:
@@ -209,7 +213,8 @@ def layernorm_rows(shape, seed):
 
 @pytest.mark.parametrize("shape,seed", [((64, 256), 81), ((2048, 4096), 82), ((100, 5120), 83),
                                         ((5, 8192), 84), ((3, 8), 85), ((777, 2048), 86),
-                                        ((40, 1000), 87), ((9, 6144), 88)])
+                                        ((40, 1000), 87), ((9, 6144), 88), ((300, 3072), 89),
+                                        ((20000, 256), 90), ((5000, 4096), 91)])
 def test_layernorm_quant(shape, seed):
     log(f"layernorm_quant {shape}")
     x = layernorm_rows(shape, seed)

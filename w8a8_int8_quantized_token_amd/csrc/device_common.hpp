@@ -33,8 +33,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, b);
 }
 
-// fp32 -> the fp32 value of its BF16 rounding (nearest even).
-__device__ __forceinline__ float round_bf16(float v) { return bf16_lo(pack_bf16x2(v, 0.0f)); }
+// fp32 -> the fp32 value of its BF16 rounding (nearest even), in one
+// instruction: with a zero low half, the packed pair is that value's bits.
+__device__ __forceinline__ float round_bf16(float v) { return __uint_as_float(pack_bf16x2(0.0f, v)); }
 
 // GELU, erf form, of a BF16 value y: y/2 * erfc(-y / sqrt(2)) in fp32. erfc
 // instead of 1 + erf keeps the digits of the small negative outputs.
@@ -154,10 +155,45 @@ __device__ __forceinline__ float quant_quotient(float x, const QuantParams& p) {
   }
 }
 
-// Low byte of the result is the INT8 code (the clamp is one v_med3_f32).
+// Low byte of the result is the INT8 code. On the reciprocal route no clamp
+// is needed: |x| <= absmax and s = fl32(absmax / 127) >= absmax / 127 /
+// (1 + 2^-24), so |x / s| <= 127 (1 + 2^-24) and its correct rounding is at
+// most 127 + 2^-17 < 127.5 for every finite x: the code is at most 127 in
+// magnitude. The division route (scales that may be subnormal, with a
+// relative error up to about 2^-9) keeps the clamp, one v_med3_f32.
+template <bool kFast>
 __device__ __forceinline__ uint32_t quant_code_bits(float t) {
-  t = __builtin_amdgcn_fmed3f(t, -127.0f, 127.0f);
+  if constexpr (!kFast) t = __builtin_amdgcn_fmed3f(t, -127.0f, 127.0f);
   return __float_as_uint(t + 12582912.0f);   // 1.5 * 2^23
+}
+
+// The codes of four quotients (clamped as quant_code_bits does) in one
+// dword. Each magic-number add is an SDWA form that writes only the low byte
+// of its sum, into byte k of the result (the other bytes kept), so the bytes
+// need no separate packing.
+template <bool kFast>
+__device__ __forceinline__ uint32_t code_bytes4(float t0, float t1, float t2, float t3) {
+  if constexpr (!kFast) {
+    t0 = __builtin_amdgcn_fmed3f(t0, -127.0f, 127.0f);
+    t1 = __builtin_amdgcn_fmed3f(t1, -127.0f, 127.0f);
+    t2 = __builtin_amdgcn_fmed3f(t2, -127.0f, 127.0f);
+    t3 = __builtin_amdgcn_fmed3f(t3, -127.0f, 127.0f);
+  }
+  const float magic = 12582912.0f;   // 1.5 * 2^23
+  uint32_t d;
+  asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD "
+      "src1_sel:DWORD"
+      : "=v"(d) : "v"(t0), "s"(magic));
+  asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD "
+      "src1_sel:DWORD"
+      : "+v"(d) : "v"(t1), "s"(magic));
+  asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD "
+      "src1_sel:DWORD"
+      : "+v"(d) : "v"(t2), "s"(magic));
+  asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD "
+      "src1_sel:DWORD"
+      : "+v"(d) : "v"(t3), "s"(magic));
+  return d;
 }
 
 // Four codes (low bytes of four code words) packed into one dword.

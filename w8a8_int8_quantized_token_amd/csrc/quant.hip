@@ -58,8 +58,8 @@ __device__ __forceinline__ uint2 quant_u4(const U4& v, const QuantParams& p) {
   const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    c[2 * i] = quant_code_bits(quant_quotient<kFast>(bf16_lo(d[i]), p));
-    c[2 * i + 1] = quant_code_bits(quant_quotient<kFast>(bf16_hi(d[i]), p));
+    c[2 * i] = quant_code_bits<kFast>(quant_quotient<kFast>(bf16_lo(d[i]), p));
+    c[2 * i + 1] = quant_code_bits<kFast>(quant_quotient<kFast>(bf16_hi(d[i]), p));
   }
   return make_uint2(pack_codes(c[0], c[1], c[2], c[3]), pack_codes(c[4], c[5], c[6], c[7]));
 }
@@ -386,16 +386,21 @@ void rmsnorm_quant_kernel(const uint16_t* __restrict__ x, const uint16_t* __rest
 // ---------------------------------------------------------------------------
 constexpr uint32_t kBf16OnePair = 0x3F803F80u;   // BF16 (1.0, 1.0)
 
-// Sum of the eight elements: each v_dot2 adds a BF16 pair (times 1), then a
-// pairwise tree.
+// Sum of the eight elements: each v_dot2 adds a BF16 pair (times 1) to its
+// accumulator; two chains of two, then one add (depth 3). The first dot of a
+// chain is written out so that its zero accumulator is the inline constant
+// (the compiler's form zeroes a register first).
+__device__ __forceinline__ float dot2_bf16_ones(uint32_t w) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(w), "s"(kBf16OnePair));
+  return r;
+}
 __device__ __forceinline__ float sum8_f32(const U4& v) {
   const auto bf = [](uint32_t d) { return __builtin_bit_cast(v2bf, d); };
   const v2bf one = bf(kBf16OnePair);
-  const float a = __builtin_amdgcn_fdot2_f32_bf16(bf(v.x), one, 0.0f, false);
-  const float b = __builtin_amdgcn_fdot2_f32_bf16(bf(v.y), one, 0.0f, false);
-  const float c = __builtin_amdgcn_fdot2_f32_bf16(bf(v.z), one, 0.0f, false);
-  const float d = __builtin_amdgcn_fdot2_f32_bf16(bf(v.w), one, 0.0f, false);
-  return (a + b) + (c + d);
+  const float a = __builtin_amdgcn_fdot2_f32_bf16(bf(v.y), one, dot2_bf16_ones(v.x), false);
+  const float b = __builtin_amdgcn_fdot2_f32_bf16(bf(v.w), one, dot2_bf16_ones(v.z), false);
+  return a + b;
 }
 
 // Sum of the eight squared deviations from mu, pairwise.
@@ -479,6 +484,232 @@ __device__ __forceinline__ U4 opt_vec(const U4* p, int idx, uint32_t identity) {
   return p ? p[idx] : U4{identity, identity, identity, identity};
 }
 
+// ---------------------------------------------------------------------------
+// Rows of up to 512 vectors (K <= 4096): the row is held as fp32 deviations
+// x - mu, formed once for the variance and reused by the normalisation, and
+// every BF16 rounding of the chain is one v_cvt_pk_bf16_f32 whose result is
+// already the rounded fp32 value (round_bf16), so no value is unpacked twice.
+// The per-channel vectors are staged in LDS as fp32 (m = bf16(1 + scale)
+// formed there), split into two 16-byte halves per 8-channel vector so each
+// ds_read_b128 of a wave reads 1 KiB of consecutive LDS.
+// ---------------------------------------------------------------------------
+constexpr int kLnF32MaxVpl = 8;
+
+// 1 / sqrt(a) in fp64: v_rsq_f64, then two Newton steps y (3 - a y^2) / 2,
+// each of which squares the relative error, for a positive finite a (zero
+// and infinity keep the first estimate, inf and 0). The result is within a
+// few fp64 ulps of the exact value, so its fp32 rounding is the correctly
+// rounded one unless the exact value lies within about 2^-50 (relative) of a
+// rounding boundary, and then it is the other neighbour.
+__device__ __forceinline__ double rsqrt_f64(double a) {
+  double y = __builtin_amdgcn_rsq(a);
+  const double h = 0.5 * a;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) y = y * __builtin_fma(-h * y, y, 1.5);
+  return (a > 0.0 && a < __builtin_inf()) ? y : __builtin_amdgcn_rsq(a);
+}
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void unpack8(const U4& v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_lo(w[i]);
+    f[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+
+// Sum of the eight squares, two fma chains of four then one add (depth 5
+// counting the first product's rounding).
+__device__ __forceinline__ float sumsq8_dev(const float (&d)[8]) {
+  float a = d[0] * d[0], b = d[4] * d[4];
+#pragma unroll
+  for (int e = 1; e < 4; ++e) {
+    a = __builtin_fmaf(d[e], d[e], a);
+    b = __builtin_fmaf(d[e + 4], d[e + 4], b);
+  }
+  return a + b;
+}
+
+// Eight fp32 values (each exactly a BF16 value) -> eight INT8 codes.
+template <bool kFast>
+__device__ __forceinline__ uint2 quant_f8(const float (&z)[8], const QuantParams& p) {
+  float t[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t[e] = quant_quotient<kFast>(z[e], p);
+  return make_uint2(code_bytes4<kFast>(t[0], t[1], t[2], t[3]),
+                    code_bytes4<kFast>(t[4], t[5], t[6], t[7]));
+}
+
+template <int kVpl, bool kFull, bool kAffine, bool kMod>
+__global__ __launch_bounds__(kLnRowsPerBlock * kWave)
+void layernorm_quant_f32_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
+                                const uint16_t* __restrict__ beta,
+                                const uint16_t* __restrict__ mod_scale,
+                                const uint16_t* __restrict__ mod_shift, float eps, int64_t rows,
+                                int64_t cols, double inv_cols, int64_t ldx,
+                                int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale,
+                                float* __restrict__ mean_out, float* __restrict__ rstd_out) {
+  static_assert(kVpl <= kLnF32MaxVpl, "fp32-resident rows hold at most 8 vectors per lane");
+  constexpr int kStaged = (kAffine ? 2 : 0) + (kMod ? 2 : 0);
+  constexpr int kSlots = kVpl * kWave;
+  // [staged vector][half][slot]: channels 8 slot + 4 half + 0..3
+  __shared__ v4f staged[kStaged > 0 ? kStaged : 1][2][kSlots];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nvec = (int)(cols >> 3);
+  // Persistent: wave w of workgroup b takes rows b * 8 + w + k * (8 * grid).
+  const int64_t stride = (int64_t)gridDim.x * kLnRowsPerBlock;
+  int64_t row = (int64_t)blockIdx.x * kLnRowsPerBlock + (threadIdx.x >> 6);
+  if constexpr (kStaged > 0) {
+    const U4* gr = reinterpret_cast<const U4*>(gamma);
+    const U4* br = reinterpret_cast<const U4*>(beta);
+    const U4* cr = reinterpret_cast<const U4*>(mod_scale);
+    const U4* hr = reinterpret_cast<const U4*>(mod_shift);
+    const auto put = [&](int t, int i, const float (&f)[8]) {
+      staged[t][0][i] = v4f{f[0], f[1], f[2], f[3]};
+      staged[t][1][i] = v4f{f[4], f[5], f[6], f[7]};
+    };
+    for (int i = threadIdx.x; i < kSlots; i += kLnRowsPerBlock * kWave) {
+      const int idx = i < nvec ? i : nvec - 1;
+      float f[8];
+      int t = 0;
+      if constexpr (kAffine) {
+        unpack8(opt_vec(gr, idx, kBf16OnePair), f);
+        put(t++, i, f);
+        unpack8(opt_vec(br, idx, 0u), f);
+        put(t++, i, f);
+      }
+      if constexpr (kMod) {
+        unpack8(opt_vec(cr, idx, 0u), f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = round_bf16(1.0f + f[e]);
+        put(t++, i, f);
+        unpack8(opt_vec(hr, idx, 0u), f);
+        put(t++, i, f);
+      }
+    }
+    __syncthreads();
+  }
+  for (; row < rows; row += stride) {
+    U4 v[kVpl];
+    load_row<kVpl, kFull>(v, reinterpret_cast<const U4*>(x + row * ldx), lane, nvec);
+    // Mean from pairwise fp32 sums (depth 3 per vector, then the vectors and
+    // the wave), then the deviations d = fl32(x - mu), whose squares give the
+    // variance; padding vectors are left out of it. Each sum is within about
+    // (log2(cols) + 7) * 2^-24 of the exact one, relative to the sum of |x|
+    // and to the sum of squares respectively. A row whose fp32 sum overflows
+    // takes its mean from an fp64 sum; one whose sum of squares overflows or
+    // falls below 2^-80 (squares in the subnormal range) sums the squares of
+    // the same deviations in fp64. Both choices are uniform over the wave and
+    // leave d where it is.
+    float part[kVpl];
+#pragma unroll
+    for (int j = 0; j < kVpl; ++j) part[j] = sum8_f32(v[j]);
+    const float s1 = wave_sum_f32(tree_sum<0, kVpl>(part));
+    float mu;
+    if (__builtin_isfinite(s1)) {
+      mu = (float)((double)s1 * inv_cols);
+    } else {
+      double s = 0.0;
+#pragma unroll
+      for (int j = 0; j < kVpl; ++j) s = sum_u4_f64(v[j], s);   // padding vectors are zero
+      mu = (float)(wave_sum_f64(s) * inv_cols);
+    }
+    float d[kVpl][8];
+#pragma unroll
+    for (int j = 0; j < kVpl; ++j) {
+      unpack8(v[j], d[j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d[j][e] -= mu;
+      part[j] = has_vec<kVpl, kFull>(lane, j, nvec) ? sumsq8_dev(d[j]) : 0.0f;
+    }
+    const float s2 = wave_sum_f32(tree_sum<0, kVpl>(part));
+    double var;
+    if (s2 >= 0x1p-80f && s2 <= 0x1p126f) {
+      var = (double)s2 * inv_cols;
+    } else {
+      double ss = 0.0;
+#pragma unroll
+      for (int j = 0; j < kVpl; ++j)
+        if (has_vec<kVpl, kFull>(lane, j, nvec))
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss = __builtin_fma((double)d[j][e], (double)d[j][e], ss);
+      var = wave_sum_f64(ss) * inv_cols;
+    }
+    const float r = (float)rsqrt_f64(var + (double)eps);
+    // normalise, affine step, modulation; the row's absmax
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kVpl; ++j) {
+      const int i = lane + j * kWave;
+      float st[kStaged > 0 ? kStaged : 1][8];
+#pragma unroll
+      for (int t = 0; t < kStaged; ++t) {
+        const v4f a = staged[t][0][i], b = staged[t][1][i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          st[t][e] = a[e];
+          st[t][e + 4] = b[e];
+        }
+      }
+      const bool in = has_vec<kVpl, kFull>(lane, j, nvec);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float u = d[j][e] * r;
+        if constexpr (kAffine) {
+          u = u * st[0][e];
+          u = u + st[1][e];
+        }
+        float y = round_bf16(u);
+        if constexpr (kMod) {
+          y = round_bf16(y * st[kAffine ? 2 : 0][e]);
+          y = round_bf16(y + st[kAffine ? 3 : 1][e]);
+        }
+        d[j][e] = in ? y : 0.0f;
+        amax = __builtin_fmaxf(amax, __builtin_fabsf(d[j][e]));
+      }
+      // keep the staged-vector reads to one vector ahead: the scheduler would
+      // otherwise hoist them all and hold them with the whole row
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // |y| as bits orders like the values (non-negative floats)
+    const QuantParams p = quant_params(__uint_as_float(wave_max_u32(__float_as_uint(amax))));
+    uint2* qr = reinterpret_cast<uint2*>(q + row * ldq);
+    if (p.fast) {
+#pragma unroll
+      for (int j = 0; j < kVpl; ++j)
+        if (has_vec<kVpl, kFull>(lane, j, nvec)) qr[lane + j * kWave] = quant_f8<true>(d[j], p);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kVpl; ++j)
+        if (has_vec<kVpl, kFull>(lane, j, nvec)) qr[lane + j * kWave] = quant_f8<false>(d[j], p);
+    }
+    if (lane == 0) {
+      scale[row] = p.s;
+      if (mean_out) mean_out[row] = mu;
+      if (rstd_out) rstd_out[row] = r;
+    }
+  }
+}
+
+// Workgroups of a persistent kernel resident at once on one CU (from its
+// registers and LDS), queried once per kernel.
+template <typename Kernel>
+static unsigned resident_per_cu(Kernel kernel, int& cache) {
+  if (cache == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kLnRowsPerBlock * kWave, 0) !=
+            hipSuccess ||
+        n < 1) {
+      (void)hipGetLastError();   // the query's failure is not the launch's
+      n = 1;
+    }
+    cache = n;
+  }
+  return (unsigned)cache;
+}
+
+// Longer rows (K up to 8192): the row stays packed as BF16 between the steps.
 template <int kVpl, bool kFull, bool kAffine, bool kMod>
 __global__ __launch_bounds__(kLnRowsPerBlock * kWave)
 void layernorm_quant_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
@@ -583,6 +814,30 @@ void layernorm_quant_kernel(const uint16_t* __restrict__ x, const uint16_t* __re
   }
 }
 
+template <int kVpl, bool kFull, bool kAffine, bool kMod>
+static void launch_layernorm_variant(dim3 grid, dim3 block, hipStream_t st, const uint16_t* x,
+                                     const uint16_t* gamma, const uint16_t* beta,
+                                     const uint16_t* mod_scale, const uint16_t* mod_shift,
+                                     float eps, int64_t rows, int64_t cols, int64_t ldx, int8_t* q,
+                                     int64_t ldq, float* scale, float* mean, float* rstd) {
+  if constexpr (kVpl <= kLnF32MaxVpl) {
+    // persistent: as many workgroups as are resident at once (from the
+    // variant's registers and LDS), each wave looping over its rows
+    static int per_cu = 0;
+    const unsigned resident =
+        resident_per_cu(layernorm_quant_f32_kernel<kVpl, kFull, kAffine, kMod>, per_cu) *
+        (unsigned)device_cu_count();
+    const dim3 pgrid(grid.x < resident ? grid.x : resident);
+    hipLaunchKernelGGL((layernorm_quant_f32_kernel<kVpl, kFull, kAffine, kMod>), pgrid, block, 0,
+                       st, x, gamma, beta, mod_scale, mod_shift, eps, rows, cols,
+                       1.0 / (double)cols, ldx, q, ldq, scale, mean, rstd);
+  }
+  else
+    hipLaunchKernelGGL((layernorm_quant_kernel<kVpl, kFull, kAffine, kMod>), grid, block, 0, st, x,
+                       gamma, beta, mod_scale, mod_shift, eps, rows, cols, ldx, q, ldq, scale,
+                       mean, rstd);
+}
+
 template <int kVpl, bool kFull>
 static hipError_t launch_layernorm(const uint16_t* x, const uint16_t* gamma, const uint16_t* beta,
                                    const uint16_t* mod_scale, const uint16_t* mod_shift,
@@ -592,9 +847,10 @@ static hipError_t launch_layernorm(const uint16_t* x, const uint16_t* gamma, con
   const dim3 grid((unsigned)((rows + kLnRowsPerBlock - 1) / kLnRowsPerBlock));
   const dim3 block(kLnRowsPerBlock * kWave);
   const bool affine = gamma || beta, mod = mod_scale || mod_shift;
-#define W8A8_LN_LAUNCH(A, M)                                                                   \
-  hipLaunchKernelGGL((layernorm_quant_kernel<kVpl, kFull, A, M>), grid, block, 0, st, x, gamma, \
-                     beta, mod_scale, mod_shift, eps, rows, cols, ldx, q, ldq, scale, mean, rstd)
+#define W8A8_LN_LAUNCH(A, M)                                                                  \
+  launch_layernorm_variant<kVpl, kFull, A, M>(grid, block, st, x, gamma, beta, mod_scale,    \
+                                              mod_shift, eps, rows, cols, ldx, q, ldq, scale, \
+                                              mean, rstd)
   if (affine && mod) W8A8_LN_LAUNCH(true, true);
   else if (affine) W8A8_LN_LAUNCH(true, false);
   else if (mod) W8A8_LN_LAUNCH(false, true);
