@@ -214,7 +214,8 @@ def layernorm_rows(shape, seed):
 @pytest.mark.parametrize("shape,seed", [((64, 256), 81), ((2048, 4096), 82), ((100, 5120), 83),
                                         ((5, 8192), 84), ((3, 8), 85), ((777, 2048), 86),
                                         ((40, 1000), 87), ((9, 6144), 88), ((300, 3072), 89),
-                                        ((20000, 256), 90), ((5000, 4096), 91)])
+                                        ((20000, 256), 90), ((5000, 4096), 91), ((60, 2560), 92),
+                                        ((50, 1536), 93), ((3000, 5120), 94), ((7, 4800), 95)])
 def test_layernorm_quant(shape, seed):
     log(f"layernorm_quant {shape}")
     x = layernorm_rows(shape, seed)

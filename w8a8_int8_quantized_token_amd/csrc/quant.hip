@@ -485,7 +485,7 @@ __device__ __forceinline__ U4 opt_vec(const U4* p, int idx, uint32_t identity) {
 }
 
 // ---------------------------------------------------------------------------
-// Rows of up to 512 vectors (K <= 4096): the row is held as fp32 deviations
+// Rows of up to 640 vectors (K <= 5120): the row is held as fp32 deviations
 // x - mu, formed once for the variance and reused by the normalisation, and
 // every BF16 rounding of the chain is one v_cvt_pk_bf16_f32 whose result is
 // already the rounded fp32 value (round_bf16), so no value is unpacked twice.
@@ -493,7 +493,11 @@ __device__ __forceinline__ U4 opt_vec(const U4* p, int idx, uint32_t identity) {
 // formed there), split into two 16-byte halves per 8-channel vector so each
 // ds_read_b128 of a wave reads 1 KiB of consecutive LDS.
 // ---------------------------------------------------------------------------
-constexpr int kLnF32MaxVpl = 8;
+constexpr int kLnF32MaxVpl = 10;
+// Rows per workgroup: 8 (two waves per SIMD), 4 for rows of 10 vectors per
+// lane, whose registers leave room for three waves per SIMD.
+template <int kVpl>
+constexpr int ln_rows_per_block() { return kVpl > 8 ? 4 : 8; }
 
 // 1 / sqrt(a) in fp64: v_rsq_f64, then two Newton steps y (3 - a y^2) / 2,
 // each of which squares the relative error, for a positive finite a (zero
@@ -541,8 +545,8 @@ __device__ __forceinline__ uint2 quant_f8(const float (&z)[8], const QuantParams
                     code_bytes4<kFast>(t[4], t[5], t[6], t[7]));
 }
 
-template <int kVpl, bool kFull, bool kAffine, bool kMod>
-__global__ __launch_bounds__(kLnRowsPerBlock * kWave)
+template <int kVpl, bool kFull, bool kAffine, bool kMod, int kRows>
+__global__ __launch_bounds__(kRows * kWave)
 void layernorm_quant_f32_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
                                 const uint16_t* __restrict__ beta,
                                 const uint16_t* __restrict__ mod_scale,
@@ -550,16 +554,16 @@ void layernorm_quant_f32_kernel(const uint16_t* __restrict__ x, const uint16_t* 
                                 int64_t cols, double inv_cols, int64_t ldx,
                                 int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale,
                                 float* __restrict__ mean_out, float* __restrict__ rstd_out) {
-  static_assert(kVpl <= kLnF32MaxVpl, "fp32-resident rows hold at most 8 vectors per lane");
+  static_assert(kVpl <= kLnF32MaxVpl, "fp32-resident rows hold at most 10 vectors per lane");
   constexpr int kStaged = (kAffine ? 2 : 0) + (kMod ? 2 : 0);
   constexpr int kSlots = kVpl * kWave;
   // [staged vector][half][slot]: channels 8 slot + 4 half + 0..3
   __shared__ v4f staged[kStaged > 0 ? kStaged : 1][2][kSlots];
   const int lane = threadIdx.x & (kWave - 1);
   const int nvec = (int)(cols >> 3);
-  // Persistent: wave w of workgroup b takes rows b * 8 + w + k * (8 * grid).
-  const int64_t stride = (int64_t)gridDim.x * kLnRowsPerBlock;
-  int64_t row = (int64_t)blockIdx.x * kLnRowsPerBlock + (threadIdx.x >> 6);
+  // Persistent: wave w of workgroup b takes rows b * kRows + w + k * (kRows * grid).
+  const int64_t stride = (int64_t)gridDim.x * kRows;
+  int64_t row = (int64_t)blockIdx.x * kRows + (threadIdx.x >> 6);
   if constexpr (kStaged > 0) {
     const U4* gr = reinterpret_cast<const U4*>(gamma);
     const U4* br = reinterpret_cast<const U4*>(beta);
@@ -569,7 +573,7 @@ void layernorm_quant_f32_kernel(const uint16_t* __restrict__ x, const uint16_t* 
       staged[t][0][i] = v4f{f[0], f[1], f[2], f[3]};
       staged[t][1][i] = v4f{f[4], f[5], f[6], f[7]};
     };
-    for (int i = threadIdx.x; i < kSlots; i += kLnRowsPerBlock * kWave) {
+    for (int i = threadIdx.x; i < kSlots; i += kRows * kWave) {
       const int idx = i < nvec ? i : nvec - 1;
       float f[8];
       int t = 0;
@@ -695,10 +699,10 @@ void layernorm_quant_f32_kernel(const uint16_t* __restrict__ x, const uint16_t* 
 // Workgroups of a persistent kernel resident at once on one CU (from its
 // registers and LDS), queried once per kernel.
 template <typename Kernel>
-static unsigned resident_per_cu(Kernel kernel, int& cache) {
+static unsigned resident_per_cu(Kernel kernel, int block, int& cache) {
   if (cache == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kLnRowsPerBlock * kWave, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block, 0) !=
             hipSuccess ||
         n < 1) {
       (void)hipGetLastError();   // the query's failure is not the launch's
@@ -823,14 +827,17 @@ static void launch_layernorm_variant(dim3 grid, dim3 block, hipStream_t st, cons
   if constexpr (kVpl <= kLnF32MaxVpl) {
     // persistent: as many workgroups as are resident at once (from the
     // variant's registers and LDS), each wave looping over its rows
+    constexpr int kRows = ln_rows_per_block<kVpl>();
     static int per_cu = 0;
     const unsigned resident =
-        resident_per_cu(layernorm_quant_f32_kernel<kVpl, kFull, kAffine, kMod>, per_cu) *
+        resident_per_cu(layernorm_quant_f32_kernel<kVpl, kFull, kAffine, kMod, kRows>,
+                        kRows * kWave, per_cu) *
         (unsigned)device_cu_count();
-    const dim3 pgrid(grid.x < resident ? grid.x : resident);
-    hipLaunchKernelGGL((layernorm_quant_f32_kernel<kVpl, kFull, kAffine, kMod>), pgrid, block, 0,
-                       st, x, gamma, beta, mod_scale, mod_shift, eps, rows, cols,
-                       1.0 / (double)cols, ldx, q, ldq, scale, mean, rstd);
+    const unsigned need = (unsigned)((rows + kRows - 1) / kRows);
+    hipLaunchKernelGGL((layernorm_quant_f32_kernel<kVpl, kFull, kAffine, kMod, kRows>),
+                       dim3(need < resident ? need : resident), dim3(kRows * kWave), 0, st, x,
+                       gamma, beta, mod_scale, mod_shift, eps, rows, cols, 1.0 / (double)cols,
+                       ldx, q, ldq, scale, mean, rstd);
   }
   else
     hipLaunchKernelGGL((layernorm_quant_kernel<kVpl, kFull, kAffine, kMod>), grid, block, 0, st, x,
@@ -952,19 +959,24 @@ hipError_t launch_layernorm_quant(const uint16_t* x, const uint16_t* gamma, cons
                                   int64_t rows, int64_t cols, int64_t ldx, int8_t* q, int64_t ldq,
                                   float* scale, float* mean, float* rstd, hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  // vectors per lane: the smallest power of two that holds the row (fewer
-  // instantiations than the quant kernels' list; other rows run masked)
+  // vectors per lane: the smallest of 1, 2, 3, 4, 5, 6, 8, 10, 12, 16 that
+  // holds the row (the common widths 1536, 2560, 3072, 4096, 5120 and 8192
+  // are exact, unpredicated rows; others run masked)
   const int64_t nvec = cols >> 3;
-  int vpl = 1;
-  while ((int64_t)vpl * kWave < nvec && vpl < kLayernormMaxVpl) vpl *= 2;
+  static const int kLnChoices[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 16};
+  int vpl = 0;
+  for (int c : kLnChoices)
+    if (vpl == 0 && nvec <= (int64_t)c * kWave) vpl = c;
   const bool full = nvec == (int64_t)vpl * kWave;
 #define W8A8_CALL_LN(V, F)                                                                  \
   launch_layernorm<V, F>(x, gamma, beta, mod_scale, mod_shift, eps, rows, cols, ldx, q, ldq, \
                          scale, mean, rstd, st)
   switch (vpl) {
     W8A8_VPL_CASE(1, W8A8_CALL_LN) W8A8_VPL_CASE(2, W8A8_CALL_LN)
-    W8A8_VPL_CASE(4, W8A8_CALL_LN) W8A8_VPL_CASE(8, W8A8_CALL_LN)
-    W8A8_VPL_CASE(16, W8A8_CALL_LN)
+    W8A8_VPL_CASE(3, W8A8_CALL_LN) W8A8_VPL_CASE(4, W8A8_CALL_LN)
+    W8A8_VPL_CASE(5, W8A8_CALL_LN) W8A8_VPL_CASE(6, W8A8_CALL_LN)
+    W8A8_VPL_CASE(8, W8A8_CALL_LN) W8A8_VPL_CASE(10, W8A8_CALL_LN)
+    W8A8_VPL_CASE(12, W8A8_CALL_LN) W8A8_VPL_CASE(16, W8A8_CALL_LN)
     default: break;
   }
 #undef W8A8_CALL_LN
