@@ -170,7 +170,9 @@ w8a8_status_t w8a8_layernorm_quant(const uint16_t* x, const uint16_t* gamma,
  *   out     [M, N] BF16, stride ldo (output)
  * Requirements (else W8A8_ERR_UNSUPPORTED_SHAPE): K % 128 == 0, 128 <= K <=
  * W8A8_MAX_K, N % 128 == 0; a, w, out 16-byte aligned; lda % 16 == 0,
- * ldw % 16 == 0, ldo % 8 == 0; scales 4-byte aligned. M >= 0 arbitrary.
+ * ldw % 16 == 0, ldo % 8 == 0; scales 4-byte aligned; 256 rows of a, of w
+ * and of out each span less than 2^31 bytes (256 lda, 256 ldw, 512 ldo <
+ * 2^31). M >= 0 arbitrary.
  *
  * This entry point always runs the single pass (one kernel). When the
  * 256 x 256 output tiles would leave most compute units idle (few tokens,
@@ -320,7 +322,8 @@ w8a8_status_t w8a8_gemm_blockwise(const int8_t* a, int64_t lda, const int8_t* w,
  * w8a8_gemm_i32 -- the post-scale GEMM's main loop with the raw INT32
  * accumulators as output (out[m,n] = sum_k a[m,k] * w[n,k]), so the integer
  * part of the path can be checked bit for bit. Same passage and requirements
- * as w8a8_gemm_postscale, with out int32 [M, N], ldo % 4 == 0.
+ * as w8a8_gemm_postscale, with out int32 [M, N], ldo % 4 == 0 (and 1024 ldo
+ * < 2^31).
  */
 w8a8_status_t w8a8_gemm_i32(const int8_t* a, int64_t lda, const int8_t* w, int64_t ldw,
                             int32_t* out, int64_t ldo,

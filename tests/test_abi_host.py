@@ -163,6 +163,8 @@ GEMM_CASES = [
     (dict(out=O + 2), UNSUPPORTED),
     (dict(lda=264), UNSUPPORTED),
     (dict(ldo=132), UNSUPPORTED),
+    (dict(lda=1 << 23), UNSUPPORTED),                               # 256 rows >= 2^31 bytes
+    (dict(ldo=1 << 22), UNSUPPORTED),                               # 256 output rows >= 2^31 bytes
     (dict(out=P), INVALID),                                         # out aliases a
 ]
 

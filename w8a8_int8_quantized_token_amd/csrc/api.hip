@@ -84,8 +84,10 @@ w8a8_status_t check_gemm_common(const int8_t* a, int64_t lda, const int8_t* w, i
   if (!a || !w || !out) return fail(W8A8_ERR_INVALID_ARGUMENT, "null pointer");
   if (!aligned(a, 16) || !aligned(w, 16) || !aligned(out, 16))
     return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "a, w and out must be 16-byte aligned");
-  // Per-tile offsets are 32-bit: 256 rows of the larger operand stride.
-  if ((int64_t)256 * (lda > ldw ? lda : ldw) > 0x7FFFFFFF)
+  // Per-tile offsets are 32-bit: 256 rows of either operand or of the
+  // output must span less than 2^31 bytes.
+  if ((int64_t)256 * (lda > ldw ? lda : ldw) > 0x7FFFFFFF ||
+      (int64_t)256 * ldo * (int64_t)out_elem > 0x7FFFFFFF)
     return fail(W8A8_ERR_UNSUPPORTED_SHAPE, "leading dimension too large");
   const size_t out_bytes = span_bytes(M, N, ldo, out_elem);
   if (overlap(out, out_bytes, a, span_bytes(M, K, lda, 1)) ||

@@ -341,6 +341,9 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
       }
     } else {
       uint16_t* o = reinterpret_cast<uint16_t*>(out);
+      // byte offset of lane (ir, kq)'s first store within its row block:
+      // token ir % 8, channels 32 (ir / 8) + 8 kq
+      const uint32_t st_lane = (uint32_t)(((ir & 7) * (int)ldo + 32 * (ir >> 3) + 8 * kq) * 2);
       // the tile's scales, brought into LDS one tile ahead
       const uint32_t sbuf = lds_addr(scale_bufs + (k % kScaleBufs) * kBufBytes);
       float sa[kTM];
@@ -421,30 +424,45 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
           // writes tokens 16 j + 0..7 and store 1 tokens 16 j + 8..15, each
           // token's 64 channels (64 hf ..) by 8 lanes. Non-temporal stores of
           // half lines cost about a third more bytes past the L2.
-          const bool lo = ir < 8;
+          // Two bank-masked DPP moves per value: store 0 keeps pk[0] in lanes
+          // 0-7 of each row and takes pk[1] of lanes 0-7 into lanes 8-15
+          // (banks 2 and 3); store 1 keeps pk[1] in lanes 8-15 and takes
+          // pk[0] of lanes 8-15 into lanes 0-7 (banks 0 and 1).
           v4u st0, st1;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const uint32_t give = lo ? pk[1][q] : pk[0][q];
-            const uint32_t got =
-                (uint32_t)__builtin_amdgcn_update_dpp(0, (int)give, 0x128, 0xF, 0xF, false);
-            st0[q] = lo ? pk[0][q] : got;
-            st1[q] = lo ? got : pk[1][q];
+            st0[q] = (uint32_t)__builtin_amdgcn_update_dpp((int)pk[0][q], (int)pk[1][q], 0x128,
+                                                           0xF, 0xC, false);
+            st1[q] = (uint32_t)__builtin_amdgcn_update_dpp((int)pk[1][q], (int)pk[0][q], 0x128,
+                                                           0xF, 0x3, false);
           }
           // Rows past M (clamped tiles only) hold exactly row M-1's sums
           // (their loads were clamped to it) and its scale, so they store row
           // M-1's values to row M-1: every lane issues its stores and the
           // per-tile store count stays fixed.
-          int m_st0 = m0 + wm * (16 * kTM) + 16 * j + (ir & 7), m_st1 = m_st0 + 8;
-          if constexpr (!kFull) {
-            m_st0 = m_st0 < M ? m_st0 : M - 1;
-            m_st1 = m_st1 < M ? m_st1 : M - 1;
-          }
-          const int col = n_wave + 64 * hf + 32 * (ir >> 3) + 8 * kq;
           // Non-temporal: the output streams past the caches instead of
           // evicting the activation and weight rows the next tiles read.
-          __builtin_nontemporal_store(st0, reinterpret_cast<v4u*>(o + (int64_t)m_st0 * ldo + col));
-          __builtin_nontemporal_store(st1, reinterpret_cast<v4u*>(o + (int64_t)m_st1 * ldo + col));
+          if constexpr (kFull) {
+            // a wave-uniform row-block address plus the lane's 32-bit offset
+            // (the host keeps 256 output rows within 2^31 bytes), so the
+            // stores take the scalar-base form with no 64-bit VALU address
+            // arithmetic
+            const char* blk = reinterpret_cast<const char*>(
+                o + ((int64_t)(m0 + wm * (16 * kTM) + 16 * j) * ldo + n_wave + 64 * hf));
+            char* b0 = const_cast<char*>(blk) + st_lane;
+            char* b1 = const_cast<char*>(blk) + 16 * ldo + st_lane;
+            __builtin_nontemporal_store(st0, reinterpret_cast<v4u*>(b0));
+            __builtin_nontemporal_store(st1, reinterpret_cast<v4u*>(b1));
+          } else {
+            int m_st0 = m0 + wm * (16 * kTM) + 16 * j + (ir & 7), m_st1 = m_st0 + 8;
+            m_st0 = m_st0 < M ? m_st0 : M - 1;
+            m_st1 = m_st1 < M ? m_st1 : M - 1;
+            const int col = n_wave + 64 * hf + 32 * (ir >> 3) + 8 * kq;
+            __builtin_nontemporal_store(st0,
+                                        reinterpret_cast<v4u*>(o + (int64_t)m_st0 * ldo + col));
+            __builtin_nontemporal_store(st1,
+                                        reinterpret_cast<v4u*>(o + (int64_t)m_st1 * ldo + col));
+          }
         }
       }
     }
