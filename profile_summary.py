@@ -84,7 +84,7 @@ def short_name(kernel: str) -> str:
         return "splitk_postscale"
     if "rmsnorm_quant_kernel" in kernel:
         return "rmsnorm_quant"
-    if "layernorm_quant_kernel" in kernel:
+    if "layernorm_quant" in kernel:
         return "layernorm_quant"
     if "quant_rows_long_kernel" in kernel:
         return "quant_rows_long"
