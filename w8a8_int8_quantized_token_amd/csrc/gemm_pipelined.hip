@@ -72,8 +72,12 @@ constexpr int kGroupM = 4;
 //  * e >= 131 (|y| >= 16): y for positive y (GELU(y) rounds to y from
 //    2.78125 on), -0 for negative y (from -13.5625 on); +inf gives +inf,
 //    -inf and NaN give NaN, as y/2 * erfc(-y / sqrt(2)) does.
-// A table index is formed for every value (clamped into the table) and the
-// entry is read; the selection then picks the entry, y/2 or the far value.
+// The values are handled in pairs, packed as they are stored (the first in
+// the low 16 bits), with 16-bit packed integer arithmetic: a clamped table
+// offset is formed for both values and both entries are read into the two
+// halves of one register; the selection then picks the entry, y/2 or the far
+// value per half. The last entry of the negative half is GELU(-15.9375) = -0,
+// so a finite negative y past the table takes its clamped entry as well.
 constexpr int kGeluFirstExp = 118;
 constexpr int kGeluHalf = 13 * 128;            // entries per sign: e = 118 .. 130
 constexpr int kGeluTable = 2 * kGeluHalf;      // entries (uint16)
@@ -86,26 +90,63 @@ __device__ __forceinline__ uint16_t gelu_table_entry(int i) {
   return (uint16_t)(pack_bf16x2(gelu_erf(y), 0.0f) & 0xFFFFu);
 }
 
-// Table index of BF16 bits; values outside the table read its last entry of
-// their sign (and discard it).
-__device__ __forceinline__ uint32_t gelu_index(uint32_t bits) {
-  const uint32_t idx = (bits & 0x7FFFu) - kGeluLow;   // wraps below the table
-  const uint32_t c = idx < (uint32_t)(kGeluHalf - 1) ? idx : (uint32_t)(kGeluHalf - 1);
-  return c + (bits >> 15) * (uint32_t)kGeluHalf;
+// Per 16-bit half of a packed BF16 pair p (magnitude bits a, sign s):
+//  * i2 = 2 (a - low) mod 2^16, computed as 2 p - 2 low (the sign bit
+//    shifts out): below the table it wraps to 0x8A00 or more, above it stays
+//    below 0x8A00 (a <= 0x7FFF);
+//  * m = 0xFFFF for negative y, else 0;
+//  * the entry's byte offset min(i2, 3326) + 3328 s (the negative half of the
+//    table follows the positive one).
+// gfx9 VOP3P encodings take no literal: the constants come in SGPRs, at most
+// one per instruction.
+struct GeluPair {
+  uint32_t i2, m, off;
+};
+__device__ __forceinline__ GeluPair gelu_pair_index(uint32_t p) {
+  GeluPair g;
+  uint32_t t0;
+  asm("v_pk_mad_u16 %[i2], %[p], 2, %[c0] op_sel_hi:[1,0,1]\n\t"
+      "v_pk_ashrrev_i16 %[m], 15, %[p] op_sel_hi:[0,1]\n\t"
+      "v_pk_min_u16 %[off], %[i2], %[c1]\n\t"
+      "v_and_b32 %[t0], 0xd000d00, %[m]\n\t"
+      "v_pk_add_u16 %[off], %[off], %[t0]"
+      : [i2] "=&v"(g.i2), [m] "=&v"(g.m), [off] "=&v"(g.off), [t0] "=&v"(t0)
+      : [p] "v"(p), [c0] "s"(0x8A008A00u), [c1] "s"(0x0CFE0CFEu));
+  return g;
 }
 
-// One BF16 GELU (bits in the low half, high half zero; bits out the same
-// way) given the table entry t read for it.
-__device__ __forceinline__ uint32_t gelu_select(uint32_t bits, uint32_t t) {
-  const uint32_t a = bits & 0x7FFFu;
-  const uint32_t idx = a - kGeluLow;
-  // the high half of the packed pair is the BF16 of +0, all zero bits
-  const uint32_t half = pack_bf16x2(__uint_as_float(bits << 16) * 0.5f, 0.0f);
-  // e >= 131: positive y (+inf included) -> y; negative finite -> -0;
-  // -inf -> NaN (0xFFC0); NaN stays NaN (its quiet bit set)
-  const uint32_t far_neg = a >= 0x7F80u ? (bits | 0x40u) : 0x8000u;
-  const uint32_t far = bits >= 0x8000u ? far_neg : bits;
-  return idx < (uint32_t)kGeluHalf ? t : (a < kGeluLow ? half : far);
+// GELU of a packed BF16 pair p given its two table entries t (packed the
+// same way), per half:
+//  * the entry where k < 0x8900, k = i2 for negative y and i2 + 0x7C01
+//    (saturating) for positive y: the table's range, and for negative y also
+//    every finite value past it (the clamped entry is -0);
+//  * below the table (i2 >= 0x8A00) the BF16 rounding of y/2 (y * 0.5 in
+//    fp32 is exact);
+//  * otherwise (positive y past the table, -inf, NaN) y with bit 6 set for
+//    negative y: +inf stays +inf, -inf gives 0xFFC0, NaNs stay quiet NaNs.
+// The two tests are the sign bits of saturating differences (k - 0x900 and
+// i2 - 0xA00), spread over the half by an arithmetic shift into bit masks
+// for v_bfi_b32.
+__device__ __forceinline__ uint32_t gelu_pair_select(uint32_t p, uint32_t t, const GeluPair& g) {
+  uint32_t r, k, b2, lo, hi;
+  asm("v_bfi_b32 %[k], %[m], 0, %[c0]\n\t"
+      "v_pk_add_u16 %[k], %[i2], %[k] clamp\n\t"
+      "v_pk_sub_u16 %[k], %[k], %[c1] clamp\n\t"
+      "v_pk_ashrrev_i16 %[k], 15, %[k] op_sel_hi:[0,1]\n\t"
+      "v_pk_sub_u16 %[b2], %[i2], %[c2] clamp\n\t"
+      "v_pk_ashrrev_i16 %[b2], 15, %[b2] op_sel_hi:[0,1]\n\t"
+      "v_lshlrev_b32 %[lo], 16, %[p]\n\t"
+      "v_and_b32 %[hi], 0xffff0000, %[p]\n\t"
+      "v_mul_f32 %[lo], 0.5, %[lo]\n\t"
+      "v_mul_f32 %[hi], 0.5, %[hi]\n\t"
+      "v_cvt_pk_bf16_f32 %[lo], %[lo], %[hi]\n\t"
+      "v_and_or_b32 %[hi], %[m], %[c3], %[p]\n\t"
+      "v_bfi_b32 %[lo], %[b2], %[lo], %[hi]\n\t"
+      "v_bfi_b32 %[r], %[k], %[lo], %[t]"
+      : [r] "=&v"(r), [k] "=&v"(k), [b2] "=&v"(b2), [lo] "=&v"(lo), [hi] "=&v"(hi)
+      : [p] "v"(p), [t] "v"(t), [i2] "v"(g.i2), [m] "v"(g.m), [c0] "s"(0x7C017C01u),
+        [c1] "s"(0x09000900u), [c2] "s"(0x0A000A00u), [c3] "s"(0x00400040u));
+  return r;
 }
 
 // 128-byte LDS rows hold 8 chunks of 16 bytes; logical chunk c of row r sits
@@ -395,15 +436,21 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
             }
             v4u packed;
             if constexpr (kGelu) {   // the FFN activation on the BF16 Linear output
-              // each value rounded to BF16 on its own (bits in the low half)
-              uint32_t y[8];
+              // the values rounded to BF16, packed in pairs as they are stored
+              uint32_t y[4];
 #pragma unroll
-              for (int e = 0; e < 8; ++e) y[e] = pack_bf16x2(v[e], 0.0f);
+              for (int q = 0; q < 4; ++q) y[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
               const uint32_t tab = lds_addr(gelu_lds);
+              // the two entries of a pair, zero-extended (16-bit loads into
+              // half a register do not keep the other half on this chip)
               uint32_t t[8];
+              GeluPair g[4];
 #pragma unroll
-              for (int e = 0; e < 8; ++e)
-                asm volatile("ds_read_u16 %0, %1" : "=v"(t[e]) : "v"(tab + 2 * gelu_index(y[e])));
+              for (int q = 0; q < 4; ++q) {
+                g[q] = gelu_pair_index(y[q]);
+                asm volatile("ds_read_u16 %0, %1" : "=v"(t[2 * q]) : "v"(tab + (g[q].off & 0xFFFFu)));
+                asm volatile("ds_read_u16 %0, %1" : "=v"(t[2 * q + 1]) : "v"(tab + (g[q].off >> 16)));
+              }
               asm volatile("s_waitcnt lgkmcnt(0)"
                            : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]),
                              "+v"(t[5]), "+v"(t[6]), "+v"(t[7])
@@ -411,8 +458,7 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
                            : "memory");
 #pragma unroll
               for (int q = 0; q < 4; ++q)
-                packed[q] = gelu_select(y[2 * q], t[2 * q]) |
-                            (gelu_select(y[2 * q + 1], t[2 * q + 1]) << 16);
+                packed[q] = gelu_pair_select(y[q], t[2 * q] | (t[2 * q + 1] << 16), g[q]);
             } else {
               packed = v4u{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                            pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
