@@ -49,7 +49,9 @@ def parse():
     # about 0.2 s of untimed steps at the default workload: the engine clock
     # needs ~150 ms of load to ramp before timing is representative
     p.add_argument("--warmup", type=int, default=100)
-    p.add_argument("--workload", default="up_proj")
+    p.add_argument("--workload", default="up_proj",
+                   help="up_proj (default), down_proj, ln_up_proj, up_proj_gelu, square, m1000, "
+                        "blockwise_small, blockwise_large, small_m or tiny (sizes in workloads/)")
     p.add_argument("--preload-ms", type=float, default=250.0,
                    help="untimed load before the timed steps: at least this much wall time "
                         "(and at least --warmup steps)")
