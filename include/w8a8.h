@@ -106,7 +106,8 @@ w8a8_status_t w8a8_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int
  *   scale   [rows] fp32                    (output)
  *   inv_rms [rows] fp32 r, or NULL         (optional output)
  * Requirements as w8a8_quant_rows with group (1, cols); gamma 16-byte aligned;
- * eps finite and >= 0 (else W8A8_ERR_INVALID_ARGUMENT).
+ * eps finite and >= 0 (else W8A8_ERR_INVALID_ARGUMENT). An all-zero row with
+ * eps = 0 has r = inf and is outside the contract.
  */
 w8a8_status_t w8a8_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps,
                                  int64_t rows, int64_t cols, int64_t ldx,

@@ -103,6 +103,29 @@ def test_gemm_postscale_gelu(shape, seed, with_bias):
     exact_report(bf16_from_dev(out), ref, "post-scale + GELU vs oracle")
 
 
+@pytest.mark.parametrize("shape,seed", [((600, 1280, 384), 158),    # 256 x 256 tiles, full-tile mode
+                                        ((70, 128, 256), 159),      # one clamped tile
+                                        ((1000, 5120, 1024), 160)]) # 128 x 160 tiles
+def test_gemm_postscale_gelu_strided_output(shape, seed):
+    """Bias + GELU into a column slice of a wider buffer: the stores follow
+    the output's row stride and the columns past N keep their contents."""
+    M, N, K = shape
+    log(f"post-scale + bias + GELU into a strided output {shape}")
+    assert w8.lib().w8a8_gemm_tile_channels(M, N, K, 0) == (160 if M == 1000 else 256)
+    qa = W.random_int8((M, K), seed)
+    qw = W.random_int8((N, K), seed + 1)
+    sa = W.random_scales((M,), seed + 2)
+    sw = W.random_scales((N,), seed + 3, lo=1e-5, hi=1e-3)
+    b = W.random_bits((N,), seed + 4, std=2.0)
+    full = torch.full((M, N + 64), -7.0, dtype=torch.bfloat16, device="cuda")
+    w8.w8a8_gemm_postscale(to_dev(qa), to_dev(qw), to_dev(sa), to_dev(sw), bias=bf16_to_dev(b),
+                           gelu=True, out=full[:, :N])
+    torch.cuda.synchronize()
+    ref = O.postscale_gelu_bf16(O.gemm_i32(qa, qw), sa, sw, b)
+    exact_report(bf16_from_dev(full[:, :N]), ref, "strided post-scale + bias + GELU vs oracle")
+    assert torch.all(full[:, N:] == -7.0)
+
+
 def test_ffn_chain_up_gelu_quant_down():
     """x -> per-token quant -> up projection + GELU -> per-token quant -> down
     projection; each step checked from the device's own inputs."""
