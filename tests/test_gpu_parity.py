@@ -73,9 +73,13 @@ def check_quant(x_bits: np.ndarray, group=(1, None), ldx_pad=0, ldq_pad=0):
         assert torch.all(qd_full[:rows, cols:] == 77)
 
 
+# Up to 2048 rows of at least 8192 columns (1024 with (1, 128) groups) run
+# several waves per row (the row's vectors spread over 2 to 16 waves, 4 to 1
+# per lane; exact or with predicated lanes); other inputs one wave per row.
 @pytest.mark.parametrize("shape,seed", [((64, 256), 1), ((3, 8), 2), ((1000, 5120), 3),
                                         ((129, 13824), 4), ((7, 20480), 5), ((333, 4096), 6),
-                                        ((16, 1032), 7)])
+                                        ((16, 1032), 7), ((100, 8200), 8), ((50, 12800), 9),
+                                        ((2048, 8192), 10), ((2049, 8192), 12), ((5, 32768), 13)])
 def test_quant_rows_per_token(shape, seed):
     log(f"quant_rows per-token {shape}")
     x = W.random_bits(shape, seed, std=1.0)
@@ -103,7 +107,8 @@ def test_quant_rows_strided():
 @pytest.mark.parametrize("shape,group,seed", [((1000, 5120), (1, 128), 21), ((37, 384), (1, 128), 22),
                                               ((200, 384), (128, 128), 23),
                                               ((5120, 1024), (128, 128), 24),
-                                              ((3, 20480), (1, 128), 25), ((1, 128), (1, 128), 26)])
+                                              ((3, 20480), (1, 128), 25), ((1, 128), (1, 128), 26),
+                                              ((40, 3200), (1, 128), 27), ((300, 1024), (1, 128), 28)])
 def test_quant_groups(shape, group, seed):
     log(f"quant_rows group {group} {shape}")
     x = W.random_bits(shape, seed)

@@ -17,6 +17,7 @@
 namespace w8a8 {
 
 constexpr int kRowsPerBlock = 4;   // 4 waves of 64 lanes, one row each
+constexpr int kMaxSplitWaves = 16; // waves per row of the few-rows kernel
 
 struct alignas(16) U4 { uint32_t x, y, z, w; };
 
@@ -140,6 +141,63 @@ void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t col
       uint32_t m = group_max_u32<16>(absmax_u4(v[j], 0u));
       const QuantParams p = quant_params(bf16_bits_to_float(m));
       if (has_vec<kVpl, kFull>(lane, j, nvec)) {
+        qr[idx] = quant_u4(v[j], p);
+        if ((lane & 15) == 0) scale[row * ngroups + (idx >> 4)] = p.s;
+      }
+    }
+  }
+}
+
+// Few rows (fewer than the chip holds waves): one workgroup of S waves per
+// row, S = blockDim.x / 64. Wave w holds vectors lane + 64 (w + S j), j <
+// kVpl, so each load still reads 1 KiB of contiguous row data; the row's
+// absmax is the maximum of the S wave maxima, exchanged through LDS. The
+// arithmetic is the per-row kernel's, so codes and scales are identical.
+// (1, 128) groups are 16 consecutive vectors, which stay in one wave.
+template <int kVpl, bool kGroup128, bool kFull>
+__global__ __launch_bounds__(kMaxSplitWaves * kWave)
+void quant_rows_split_kernel(const uint16_t* __restrict__ x, int64_t cols, int64_t ldx,
+                             int8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale) {
+  __shared__ uint32_t wave_max[kMaxSplitWaves];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x >> 6;
+  const int S = blockDim.x >> 6;
+  const int64_t row = blockIdx.x;
+  const int nvec = (int)(cols >> 3);
+  const U4* xr = reinterpret_cast<const U4*>(x + row * ldx);
+  uint2* qr = reinterpret_cast<uint2*>(q + row * ldq);
+  U4 v[kVpl];
+#pragma unroll
+  for (int j = 0; j < kVpl; ++j) {
+    const int idx = lane + kWave * (w + S * j);
+    const U4 t = load_nt(xr + (kFull || idx < nvec ? idx : nvec - 1));
+    const bool in = kFull || idx < nvec;
+    v[j] = U4{in ? t.x : 0u, in ? t.y : 0u, in ? t.z : 0u, in ? t.w : 0u};
+  }
+  if constexpr (!kGroup128) {
+    uint32_t m2 = 0;
+#pragma unroll
+    for (int j = 0; j < kVpl; ++j) m2 = absmax2_u4(v[j], m2);
+    const uint32_t mw = wave_max_u32(fold_absmax(m2));
+    if (lane == 0) wave_max[w] = mw;
+    __syncthreads();
+    uint32_t m = 0;
+    for (int i = 0; i < S; ++i) m = umax(m, wave_max[i]);
+    const QuantParams p = quant_params(bf16_bits_to_float(m));
+#pragma unroll
+    for (int j = 0; j < kVpl; ++j) {
+      const int idx = lane + kWave * (w + S * j);
+      if (kFull || idx < nvec) qr[idx] = quant_u4(v[j], p);
+    }
+    if (threadIdx.x == 0) scale[row] = p.s;
+  } else {
+    const int64_t ngroups = cols >> 7;
+#pragma unroll
+    for (int j = 0; j < kVpl; ++j) {
+      const int idx = lane + kWave * (w + S * j);
+      const uint32_t m = group_max_u32<16>(absmax_u4(v[j], 0u));
+      const QuantParams p = quant_params(bf16_bits_to_float(m));
+      if (kFull || idx < nvec) {
         qr[idx] = quant_u4(v[j], p);
         if ((lane & 15) == 0) scale[row * ngroups + (idx >> 4)] = p.s;
       }
@@ -896,6 +954,32 @@ static int pick_vpl(int64_t nvec) {
   return 0;
 }
 
+// The few-rows kernel: up to kSplitRowsMax rows (fewer than 4 waves per SIMD
+// with one wave per row). Per-token rows take it from 1024 vectors (8192
+// columns) on, where one wave's chain over the row is long; below that it
+// gains nothing (graph-replayed on MI355X: 1000 x 5120 in 3.5 us either way,
+// 256 x 13824 in 5.1 us one wave per row against 3.2 us, 1000 x 8192 5.6
+// against 4.6 us). (1, 128) groups need no barrier and take it from 128
+// vectors on (1000 x 5120: 4.5 against 3.6 us). Its shape: the fewest waves
+// per row (2 to 16) whose vectors-per-lane count, 4 down to 1, covers the row
+// exactly (10 waves of 1 vector took 6.4 us at 1000 x 5120, 5 waves of 2
+// about the single-wave time), else 8 waves with the predicated variant.
+constexpr int64_t kSplitRowsMax = 2048;
+struct SplitShape {
+  int waves, vpl;
+  bool full;
+};
+static SplitShape pick_split(int64_t nvec, bool g128) {
+  if (nvec < (g128 ? 2 : 16) * kWave || nvec > (int64_t)kMaxSplitWaves * 4 * kWave)
+    return {0, 0, false};
+  for (int v = 4; v >= 1; --v)
+    for (int wv = 2; wv <= kMaxSplitWaves; ++wv)
+      if ((int64_t)wv * v * kWave == nvec) return {wv, v, true};
+  const int64_t per = 8 * kWave;
+  const int v = (int)((nvec + per - 1) / per);
+  return v <= 4 ? SplitShape{8, v, false} : SplitShape{0, 0, false};
+}
+
 #define W8A8_VPL_CASE(V, CALL) \
   case V: return full ? CALL(V, true) : CALL(V, false);
 #define W8A8_VPL_SWITCH(VPL, CALL)                                                   \
@@ -921,6 +1005,29 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t cols, int6
   }
   // (1, 128) on a 128-wide matrix is the same as one group per row
   const bool g128 = group_cols == 128 && cols != 128;
+  if (rows <= kSplitRowsMax) {
+    const SplitShape sp = pick_split(cols >> 3, g128);
+    if (sp.waves > 0) {
+#define W8A8_SPLIT(V, G, F)                                                                  \
+  hipLaunchKernelGGL((quant_rows_split_kernel<V, G, F>), dim3((unsigned)rows),               \
+                     dim3(sp.waves * kWave), 0, st, x, cols, ldx, q, ldq, scale);             \
+  return hipGetLastError();
+#define W8A8_SPLIT_F(V, G) \
+  if (sp.full) { W8A8_SPLIT(V, G, true) } else { W8A8_SPLIT(V, G, false) }
+#define W8A8_SPLIT_G(V) \
+  if (g128) { W8A8_SPLIT_F(V, true) } else { W8A8_SPLIT_F(V, false) }
+      switch (sp.vpl) {
+        case 1: { W8A8_SPLIT_G(1) }
+        case 2: { W8A8_SPLIT_G(2) }
+        case 3: { W8A8_SPLIT_G(3) }
+        case 4: { W8A8_SPLIT_G(4) }
+        default: break;
+      }
+#undef W8A8_SPLIT_G
+#undef W8A8_SPLIT_F
+#undef W8A8_SPLIT
+    }
+  }
   const int vpl = pick_vpl(cols >> 3);
   const bool full = vpl > 0 && (cols >> 3) == (int64_t)vpl * kWave;
   if (!g128) {
