@@ -88,6 +88,11 @@ def short_name(kernel: str) -> str:
         return "layernorm_quant"
     if "quant_rows_long_kernel" in kernel:
         return "quant_rows_long"
+    if "quant_rows_split_kernel" in kernel:
+        # quant_rows_split_kernel<vectors per lane, 128-wide groups?, full rows?>:
+        # the few-rows form, several waves per row
+        m = re.search(r"quant_rows_split_kernel<\d+, (true|false)", kernel)
+        return "quant_rows_1x128_split" if m and m.group(1) == "true" else "quant_rows_split"
     if "quant_rows_kernel" in kernel:
         # quant_rows_kernel<vectors per lane, 128-wide groups?, full rows?>
         m = re.search(r"quant_rows_kernel<\d+, (true|false)", kernel)
