@@ -103,6 +103,28 @@ def test_rmsnorm_quant_rejects(kwargs, status):
     assert rms(**kwargs) == status
 
 
+def test_last_error_is_per_thread():
+    # the description of a failed call belongs to the calling thread: another
+    # thread starts with none and its own failures leave this one's untouched
+    import threading
+    assert quant(x=None) == INVALID
+    mine = w8.lib().w8a8_last_error()
+    assert mine != b""
+    seen = {}
+
+    def other():
+        seen["before"] = w8.lib().w8a8_last_error()
+        seen["status"] = rms(gamma=None)
+        seen["after"] = w8.lib().w8a8_last_error()
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["before"] == b"" and seen["status"] == INVALID
+    assert seen["after"] != b"" and seen["after"] != mine
+    assert w8.lib().w8a8_last_error() == mine
+
+
 def ln(x=P, gamma=0x30000000, beta=0x30100000, sc=0x30200000, sh=0x30300000, eps=1e-6, rows=8,
        cols=256, ldx=256, q=Q, ldq=256, s=S, mean=0x70000000, rstd=0x70100000):
     return w8.lib().w8a8_layernorm_quant(x, gamma, beta, sc, sh, eps, rows, cols, ldx, q, ldq, s,

@@ -40,6 +40,8 @@
 //    16 lanes at a time and is conflict-free when those lanes hit 16
 //    distinct 16-byte slots of the 256-byte bank line; the keys below give
 //    every such lane group of the fragment reads distinct slots.
+#include <atomic>
+
 #include "launch.hpp"
 #include "pipeline.hpp"
 
@@ -591,17 +593,20 @@ void gemm_i8_pipelined(const int8_t* __restrict__ a, int64_t lda, const int8_t* 
 
 }  // namespace pipe
 
+// Compute units of the current device, queried once per device. Calls from
+// several host threads may race to fill an entry; they store the same value,
+// and the entries are atomics so that this is well defined.
 int device_cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 hipError_t launch_gemm_pipelined(Epilogue epi, const int8_t* a, int64_t lda, const int8_t* w,

@@ -11,6 +11,8 @@
 // stays in registers between the absmax reduction and the quantisation, so
 // HBM sees it exactly once. Rows longer than the register budget fall back to
 // a two-pass loop that re-reads the row (from L2).
+#include <atomic>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -755,20 +757,21 @@ void layernorm_quant_f32_kernel(const uint16_t* __restrict__ x, const uint16_t* 
 }
 
 // Workgroups of a persistent kernel resident at once on one CU (from its
-// registers and LDS), queried once per kernel.
+// registers and LDS), queried once per kernel. Host threads may race to fill
+// the cache with the same value; it is an atomic so that this is well defined.
 template <typename Kernel>
-static unsigned resident_per_cu(Kernel kernel, int block, int& cache) {
-  if (cache == 0) {
-    int n = 0;
+static unsigned resident_per_cu(Kernel kernel, int block, std::atomic<int>& cache) {
+  int n = cache.load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block, 0) !=
             hipSuccess ||
         n < 1) {
       (void)hipGetLastError();   // the query's failure is not the launch's
       n = 1;
     }
-    cache = n;
+    cache.store(n, std::memory_order_relaxed);
   }
-  return (unsigned)cache;
+  return (unsigned)n;
 }
 
 // Longer rows (K up to 8192): the row stays packed as BF16 between the steps.
@@ -886,7 +889,7 @@ static void launch_layernorm_variant(dim3 grid, dim3 block, hipStream_t st, cons
     // persistent: as many workgroups as are resident at once (from the
     // variant's registers and LDS), each wave looping over its rows
     constexpr int kRows = ln_rows_per_block<kVpl>();
-    static int per_cu = 0;
+    static std::atomic<int> per_cu{0};
     const unsigned resident =
         resident_per_cu(layernorm_quant_f32_kernel<kVpl, kFull, kAffine, kMod, kRows>,
                         kRows * kWave, per_cu) *
