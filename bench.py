@@ -225,6 +225,41 @@ def mainloop_ceiling() -> None:
                       "peak_tops": 5000.0, "results": res["results"]}), flush=True)
 
 
+def rel_error_vs_fp32_linear(wl, x, w, gamma, mod_scale, mod_shift, bias, out) -> float:
+    """Relative Frobenius error of the W8A8 step's BF16 output against a
+    float32 Linear (torch, on the GPU) of the same unquantised BF16 input:
+    after the step's norm prologue, rounded to BF16 as the fused kernels do
+    before quantising, with the bias and the GELU (erf form) where the step
+    has them. An informational figure of the quantisation noise, not a parity
+    check (the parity tests compare with the oracle)."""
+    import torch
+    xf = x.float()
+    if wl.norm:
+        r = torch.rsqrt(xf.double().square().mean(1, keepdim=True) + wl.eps).float()
+        y = ((xf * r) * gamma.float()).bfloat16().float()
+    elif wl.layernorm:
+        xd = xf.double()
+        mu = xd.mean(1, keepdim=True)
+        r = torch.rsqrt((xd - mu).square().mean(1, keepdim=True) + wl.eps).float()
+        y = ((xf - mu.float()) * r).bfloat16().float()
+        y = (y * (1.0 + mod_scale.float()).bfloat16().float()).bfloat16().float()
+        y = (y + mod_shift.float()).bfloat16().float()
+    else:
+        y = xf
+    del xf
+    ref = torch.nn.functional.linear(y, w.float())
+    del y
+    if bias is not None:
+        ref += bias.float()
+    if wl.gelu:
+        ref = torch.nn.functional.gelu(ref)
+    err = float(torch.linalg.vector_norm((out.float() - ref).double()))
+    rel = err / float(torch.linalg.vector_norm(ref.double()))
+    del ref
+    torch.cuda.empty_cache()
+    return round(rel, 5)
+
+
 def source_hash(*names) -> str:
     h = hashlib.sha256()
     for n in names:
@@ -476,6 +511,10 @@ def main():
         bf16_ms = e0.elapsed_time(e1) / reps
         extra["torch_bf16_linear_ms"] = round(bf16_ms, 4)
         extra["speedup_vs_bf16_linear"] = round(bf16_ms / float(step_ms.mean()), 3)
+        # informational accuracy of the step's output (every rotated input
+        # holds the same values, so `out` is the W8A8 Linear of xs[0])
+        extra["rel_frobenius_error_vs_fp32_linear"] = rel_error_vs_fp32_linear(
+            wl, xs[0], w_bf16, gamma, mod_scale, mod_shift, bias, out)
 
     # ---- the post-scale kernel's own main loop on this GPU, as a yardstick
     # for roofline.frac (the chip's power limit caps it on random operands) --
