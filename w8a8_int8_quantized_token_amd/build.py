@@ -12,10 +12,12 @@ denormals kept, and no packed-fp32 VALU instructions.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -51,20 +53,35 @@ def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _link(srcs: list[str], includes: list[str], out: str, verbose: bool) -> str:
-    tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS]
-    for inc in includes:
-        cmd += ["-I", inc]
-    cmd += [*srcs, "-o", tmp]
+def _run(cmd: list[str], what: str, verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building " + os.path.basename(out))
+        raise RuntimeError("hipcc failed building " + what)
     if verbose and res.stderr.strip():
         sys.stderr.write(res.stderr)
+
+
+def _link(srcs: list[str], includes: list[str], out: str, verbose: bool) -> str:
+    """Compile every source to an object of its own (in parallel: each
+    translation unit carries its own device code, and none calls device code
+    of another), then link the shared library."""
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    inc = [a for i in includes for a in ("-I", i)]
+    tmp = out + ".tmp"
+    with tempfile.TemporaryDirectory(prefix="w8a8_build_") as objdir:
+        objs = [os.path.join(objdir, f"{i}_{os.path.basename(s)}.o") for i, s in enumerate(srcs)]
+        jobs = max(1, min(len(srcs), os.cpu_count() or 1, 8))
+        with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as pool:
+            futures = [pool.submit(_run, [hipcc(), *compile_flags, *inc, "-c", s, "-o", o],
+                                   os.path.basename(s), verbose)
+                       for s, o in zip(srcs, objs)]
+            for f in futures:
+                f.result()
+        _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
+             os.path.basename(out), verbose)
     os.replace(tmp, out)
     return out
 
