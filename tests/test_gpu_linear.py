@@ -161,3 +161,89 @@ def test_int8_linear_gelu_activation():
     assert not fb.int8
     xs = bf16_to_dev(W.random_bits((7, 256), 175))
     assert torch.equal(fb(xs), torch.nn.functional.gelu(torch.nn.functional.linear(xs, fb.weight)))
+
+
+# ---- NormInt8Linear: a norm fused with the Int8Linear's activation quant ----
+
+def _norm_linear(norm, K, N, seed, affine=True):
+    w = W.random_bits((N, K), seed, std=0.02)
+    b = W.random_bits((N,), seed + 1, std=0.1)
+    g = W.random_bits((K,), seed + 2, std=0.1, mean=1.0)
+    beta = W.random_bits((K,), seed + 3, std=0.1) if (affine and norm == "layernorm") else None
+    lin = w8.Int8Linear(bf16_to_dev(w), bf16_to_dev(b))
+    gamma = g if (affine or norm == "rmsnorm") else None
+    mod = w8.NormInt8Linear(lin, norm, None if gamma is None else bf16_to_dev(gamma),
+                            None if beta is None else bf16_to_dev(beta), eps=1e-6)
+    return mod, w, b, gamma, beta
+
+
+@pytest.mark.parametrize("norm,affine,modulated", [("rmsnorm", True, False),
+                                                   ("layernorm", True, True),
+                                                   ("layernorm", False, True),
+                                                   ("layernorm", True, False)])
+def test_norm_int8_linear_matches_oracle(norm, affine, modulated):
+    # the fused path: codes from the device's statistics, then the exact
+    # GEMM and the bias epilogue, all bit for bit
+    K, N = 512, 384
+    log(f"NormInt8Linear {norm} affine={affine} modulated={modulated}")
+    mod, w, b, g, beta = _norm_linear(norm, K, N, 301, affine)
+    x = W.random_bits((2, 50, K), 305, std=1.5, mean=0.2)
+    sc = W.random_bits((K,), 306, std=0.2) if modulated else None
+    sh = W.random_bits((K,), 307, std=0.2) if modulated else None
+    xd = bf16_to_dev(x)
+    out = mod(xd, None if sc is None else bf16_to_dev(sc), None if sh is None else bf16_to_dev(sh))
+    x2 = x.reshape(-1, K)
+    if norm == "rmsnorm":
+        _, _, r = w8.w8a8_rmsnorm_quant(bf16_to_dev(x2), bf16_to_dev(g), 1e-6)
+        torch.cuda.synchronize()
+        qa, sa, _ = O.rmsnorm_quant(x2, g, 1e-6, r=from_dev(r))
+    else:
+        _, _, mu, r = w8.w8a8_layernorm_quant(
+            bf16_to_dev(x2), 1e-6, *[None if t is None else bf16_to_dev(t) for t in (g, beta, sc, sh)])
+        torch.cuda.synchronize()
+        qa, sa, _, _ = O.layernorm_quant(x2, 1e-6, g, beta, sc, sh, mu=from_dev(mu), r=from_dev(r))
+    qw, sw = O.quantize_rows(w)
+    ref = O.postscale_bias_bf16(O.gemm_i32(qa, qw), sa, sw, b)
+    assert out.shape == (2, 50, N)
+    exact_check(bf16_from_dev(out).reshape(-1, N), ref, f"{norm} module")
+
+
+def test_norm_int8_linear_torch_norm_where_the_fused_kernel_does_not_fit():
+    # LayerNorm rows longer than the fused kernels take (K = 8320): the norm
+    # and modulation run as torch operations, then the Int8Linear quantises
+    # their BF16 output; against the oracle with its own statistics
+    K, N = 8320, 256
+    log("NormInt8Linear layernorm at K = 8320 (torch norm, INT8 Linear)")
+    mod, w, b, g, beta = _norm_linear("layernorm", K, N, 311)
+    x = W.random_bits((40, K), 315, std=1.0)
+    sc = W.random_bits((K,), 316, std=0.2)
+    sh = W.random_bits((K,), 317, std=0.2)
+    out = mod(bf16_to_dev(x), bf16_to_dev(sc), bf16_to_dev(sh))
+    mu, r = O.layernorm_stats(x, 1e-6)
+    y = O.modulate_bf16(O.layernorm_bf16(x, mu, r, g, beta), sc, sh)
+    qa, sa = O.quantize_rows(y)
+    qw, sw = O.quantize_rows(w)
+    ref = O.postscale_bias_bf16(O.gemm_i32(qa, qw), sa, sw, b)
+    exact_check(bf16_from_dev(out), ref, "torch norm + INT8 Linear")
+
+
+def test_norm_int8_linear_bf16_fallback_and_argument_errors():
+    # a weight the INT8 GEMM does not take (K = 200): torch's RMSNorm steps,
+    # then torch's BF16 Linear
+    K, N = 200, 128
+    mod, w, b, g, _ = _norm_linear("rmsnorm", K, N, 321)
+    assert not mod.linear.int8
+    x = W.random_bits((30, K), 325)
+    out = mod(bf16_to_dev(x))
+    y = O.rmsnorm_bf16(x, g, O.rmsnorm_inv_rms(x, 1e-6))
+    ref = torch.nn.functional.linear(bf16_to_dev(y), bf16_to_dev(w), bf16_to_dev(b))
+    assert torch.equal(out, ref)
+    lin = w8.Int8Linear(bf16_to_dev(w), bf16_to_dev(b))
+    with pytest.raises(w8.W8A8Error):
+        w8.NormInt8Linear(lin, "rmsnorm")                       # RMSNorm needs its gain
+    with pytest.raises(w8.W8A8Error):
+        w8.NormInt8Linear(lin, "batchnorm")
+    with pytest.raises(w8.W8A8Error):
+        mod(bf16_to_dev(x), mod_scale=bf16_to_dev(g))          # modulation follows LayerNorm only
+    with pytest.raises(w8.W8A8Error):
+        mod(bf16_to_dev(x).float())

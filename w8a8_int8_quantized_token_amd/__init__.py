@@ -19,7 +19,7 @@ __all__ = [
     "w8a8_quant_rows", "w8a8_rmsnorm_quant", "w8a8_layernorm_quant", "w8a8_gemm_postscale",
     "w8a8_gemm_blockwise", "w8a8_gemm_i32", "w8a8_version", "splitk_parts",
     "w8a8_gemm_postscale_noalloc", "tile_channels",
-    "postscale_workspace_size", "Int8Linear",
+    "postscale_workspace_size", "Int8Linear", "NormInt8Linear",
     "replace_linear_with_int8",
 ]
 
@@ -381,4 +381,4 @@ def w8a8_gemm_i32(a: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = N
     return out
 
 
-from .linear import Int8Linear, replace_linear_with_int8  # noqa: E402  (needs the binding above)
+from .linear import Int8Linear, NormInt8Linear, replace_linear_with_int8  # noqa: E402  (needs the binding above)

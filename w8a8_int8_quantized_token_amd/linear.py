@@ -17,7 +17,8 @@ from __future__ import annotations
 import torch
 
 from . import W8A8Error, W8A8Unsupported, W8A8_ERR_INVALID_ARGUMENT, W8A8_MAX_K
-from . import w8a8_gemm_postscale, w8a8_quant_rows
+from . import (w8a8_gemm_postscale, w8a8_layernorm_quant, w8a8_quant_rows,
+               w8a8_rmsnorm_quant)
 
 
 def int8_shape_supported(out_features: int, in_features: int) -> bool:
@@ -83,6 +84,100 @@ class Int8Linear(torch.nn.Module):
                 pass
         y = torch.nn.functional.linear(x, self.weight, self.bias)
         return torch.nn.functional.gelu(y) if self.activation == "gelu" else y
+
+
+class NormInt8Linear(torch.nn.Module):
+    """A norm followed by an Int8Linear, with the norm fused into the
+    Linear's per-token activation quant.
+
+    "Reused Components", FastNorm and W8A8 Linear bullets: the norms and the
+    Linear are separate reused modules; here the normalised BF16 row is
+    quantised where it is formed and never reaches memory, which gives the
+    same codes as the norm module (BF16 out) followed by the Int8Linear.
+
+    norm="rmsnorm": y = bf16((x r) g), r = 1 / sqrt(mean x^2 + eps), g the
+    gain (`weight`, required). norm="layernorm": y = bf16(((x - mu) r) g + b)
+    with `weight` and `bias` optional, then, if forward() gets them, the adaLN
+    modulation bf16(bf16(y bf16(1 + mod_scale)) + mod_shift). Where the fused
+    kernels do not take the shape, the same steps run as torch operations on
+    the GPU, in fp32 with the statistics in fp64, each BF16 rounding where the
+    fused kernels round, and `linear` then runs on their BF16 output as usual.
+    """
+
+    def __init__(self, linear: Int8Linear, norm: str, weight: torch.Tensor | None = None,
+                 bias: torch.Tensor | None = None, eps: float = 1e-6):
+        super().__init__()
+        if not isinstance(linear, Int8Linear):
+            raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, "NormInt8Linear wraps an Int8Linear")
+        if norm not in ("rmsnorm", "layernorm"):
+            raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, f"unknown norm {norm!r}")
+        if norm == "rmsnorm" and (weight is None or bias is not None):
+            raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, "RMSNorm takes a gain and no bias")
+        self.linear = linear
+        self.norm = norm
+        self.eps = float(eps)
+        dev = linear.weight.device
+        k = linear.in_features
+        for name, t in (("norm_weight", weight), ("norm_bias", bias)):
+            if t is not None and t.numel() != k:
+                raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, f"{name} must have {k} elements")
+            self.register_buffer(name, None if t is None else
+                                 t.detach().to(device=dev, dtype=torch.bfloat16).reshape(k)
+                                 .contiguous())
+
+    def extra_repr(self) -> str:
+        return f"norm={self.norm}, eps={self.eps}"
+
+    def _norm_torch(self, x: torch.Tensor, mod_scale, mod_shift) -> torch.Tensor:
+        xf = x.float()
+        eps = torch.tensor(self.eps, dtype=torch.float32).item()   # the fp32 eps
+        if self.norm == "rmsnorm":
+            r = (1.0 / torch.sqrt(xf.double().square().mean(-1, keepdim=True) + eps)).float()
+            return ((xf * r) * self.norm_weight.float()).bfloat16()
+        xd = xf.double()
+        mu = xd.mean(-1, keepdim=True)
+        r = (1.0 / torch.sqrt((xd - mu).square().mean(-1, keepdim=True) + eps)).float()
+        u = (xf - mu.float()) * r
+        if self.norm_weight is not None:
+            u = u * self.norm_weight.float()
+        if self.norm_bias is not None:
+            u = u + self.norm_bias.float()
+        y = u.bfloat16()
+        if mod_scale is not None:
+            y = (y.float() * (1.0 + mod_scale.float()).bfloat16().float()).bfloat16()
+        if mod_shift is not None:
+            y = (y.float() + mod_shift.float()).bfloat16()
+        return y
+
+    def forward(self, x: torch.Tensor, mod_scale: torch.Tensor | None = None,
+                mod_shift: torch.Tensor | None = None) -> torch.Tensor:
+        if x.device.type != "cuda":
+            raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, "NormInt8Linear runs on the GPU only")
+        if x.dtype != torch.bfloat16:
+            raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, "NormInt8Linear takes BF16 activations")
+        if self.norm == "rmsnorm" and (mod_scale is not None or mod_shift is not None):
+            raise W8A8Error(W8A8_ERR_INVALID_ARGUMENT, "the modulation follows a LayerNorm")
+        lin = self.linear
+        k = lin.in_features
+        mods = [None if t is None else t.to(torch.bfloat16).reshape(k).contiguous()
+                for t in (mod_scale, mod_shift)]
+        if lin.int8:
+            x2 = x.reshape(-1, k)
+            if not x2.is_contiguous():
+                x2 = x2.contiguous()
+            try:
+                if self.norm == "rmsnorm":
+                    qa, sa, _ = w8a8_rmsnorm_quant(x2, self.norm_weight, self.eps, inv_rms=False)
+                else:
+                    qa, sa, _, _ = w8a8_layernorm_quant(x2, self.eps, self.norm_weight,
+                                                        self.norm_bias, mods[0], mods[1],
+                                                        stats=False)
+                out = w8a8_gemm_postscale(qa, lin.qweight, sa, lin.weight_scale, bias=lin.bias,
+                                          gelu=lin.activation == "gelu")
+                return out.reshape(*x.shape[:-1], lin.out_features)
+            except W8A8Unsupported:
+                pass
+        return lin(self._norm_torch(x, mods[0], mods[1]))
 
 
 def replace_linear_with_int8(module: torch.nn.Module, select=None) -> int:
